@@ -1,0 +1,117 @@
+"""ORACLE -- test infrastructure only.
+
+A plain double-precision CPU definition of sparse latent attention with a
+per-head attention sink (the C source ``sparse_attn_ref.c`` beside this file
+states the definition and the passages it follows).  Only the tests, the smoke
+check and the benchmark's CPU-baseline leg import this package.  It shares no
+code with the GPU library in ``sparse_top_latent_amd`` and imports nothing
+from it.
+
+``build()`` compiles the C source with gcc (-O2, OpenMP, no fast-math);
+``sparse_attn_ref`` calls it through ctypes on numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sparse_attn_ref.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into ``oracle/liboracle.so`` and return its path."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall",
+             "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_sparse_attn_f64.argtypes = [P, P, P, P, ctypes.c_float,
+                                           I64, I64, I64, I64, I64, I64, P, P, P]
+    lib.oracle_sparse_attn_f64.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS or all cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def sparse_attn_ref(q_bits, kv_bits, sink, idxs, scale, *, weights: bool = False):
+    return _call(_load(), q_bits, kv_bits, sink, idxs, scale, weights)
+
+
+def ref_from_library(path):
+    """The same interface over another build of the oracle's C entry point
+    (the tests use it to run the pins against planted mistakes)."""
+    lib = _bind(path)
+
+    def fn(q_bits, kv_bits, sink, idxs, scale, *, weights: bool = False):
+        return _call(lib, q_bits, kv_bits, sink, idxs, scale, weights)
+    return fn
+
+
+def _call(lib, q_bits, kv_bits, sink, idxs, scale, weights):
+    """fp64 sparse attention with a sink.
+
+    q_bits  : uint16 bf16 bit patterns [B, T, H, D]
+    kv_bits : uint16 bf16 bit patterns [B, N, D]
+    sink    : float32 [H] or None (no sink)
+    idxs    : int32 [B, T, K]; negative entries are unused
+    scale   : Python float, rounded to float32 as the GPU boundary receives it
+    Returns out [B, T, H, D] float64, plus (w [B,T,H,K], w_sink [B,T,H]) when
+    ``weights`` is true.  Raises ValueError on an index >= N.
+    """
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    kv_bits = np.ascontiguousarray(kv_bits, dtype=np.uint16)
+    idxs = np.ascontiguousarray(idxs, dtype=np.int32)
+    if sink is not None:
+        sink = np.ascontiguousarray(sink, dtype=np.float32)
+    B, T, H, D = q_bits.shape
+    Bk, N, Dk = kv_bits.shape
+    Bi, Ti, K = idxs.shape
+    if (Bk, Dk) != (B, D) or (Bi, Ti) != (B, T):
+        raise ValueError("shape mismatch between q, kv and idxs")
+    if sink is not None and sink.shape != (H,):
+        raise ValueError("sink must have shape [H]")
+    out = np.zeros((B, T, H, D), dtype=np.float64)
+    w = np.zeros((B, T, H, K), dtype=np.float64) if weights else None
+    ws = np.zeros((B, T, H), dtype=np.float64) if weights else None
+    rc = lib.oracle_sparse_attn_f64(
+        _ptr(q_bits), _ptr(kv_bits), _ptr(sink), _ptr(idxs), ctypes.c_float(scale),
+        B, T, H, D, N, K, _ptr(out), _ptr(w), _ptr(ws))
+    if rc == 1:
+        raise ValueError("index list holds an entry >= N")
+    if rc != 0:
+        raise ValueError(f"oracle rejected the dimensions (code {rc})")
+    if weights:
+        return out, w, ws
+    return out
