@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse latent attention step on one MI355X.
+
+Workload: the DeepSeek-V4.1 decode batch (B=64 sequences, one query each,
+H=64 heads of width 512, K=640 list entries = 128 window rows + 512 distinct
+compressed rows out of 8192, scale 512^-0.5), synthetic and seeded.
+
+A step is one pass of the whole path over the batch: index decode, gather,
+QK^T, sink softmax, PV and (with splits) the log-sum-exp combine.  Inputs are
+resident in HBM before timing; the timed steps cycle through ``--rotate``
+copies of q/kv/idxs at distinct addresses so that the rows a step gathers are
+not still sitting in the 256 MB Infinity Cache from the previous step (a
+second, labelled figure runs with one copy).  Each step is replayed from a
+captured HIP graph so that host launch overhead is not part of the time.
+
+Prints one JSON line.  ``value`` = queries per second.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fwd_decode_counters.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "sparse_top_latent_amd", "csrc", "sparse_attn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=8, help="input copies cycled by the steps")
+    ap.add_argument("--workload", default="decode",
+                    help="decode (the benchmark line) or another generator name")
+    ap.add_argument("--splits", type=int, default=0, help="0 = planned by the library")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run plain 256 MiB copies first (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def read_counters():
+    """HBM bytes per launch of the main kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def gate(torch, ms=20.0):
+    """Keep the GPU busy for a moment so the host can queue the timed work."""
+    torch.cuda._sleep(int(ms * 1e-3 * 2.1e9))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_top_latent_amd import api, workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = wl.make(args.workload)
+    R = max(1, args.rotate)
+    q0 = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kv0 = w.kv_device(dev)
+    idx0 = torch.from_numpy(w.idxs).to(dev)
+    sink = torch.from_numpy(w.sink).to(dev)
+    qs = [q0] + [q0.clone() for _ in range(R - 1)]
+    kvs = [kv0] + [kv0.clone() for _ in range(R - 1)]
+    idxs = [idx0] + [idx0.clone() for _ in range(R - 1)]
+    out = torch.empty_like(q0)
+    S = args.splits if args.splits > 0 else api.plan_splits(q0, kv0, idx0)
+    ws_bytes = api.workspace_bytes(q0, kv0, idx0, S)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    if args.copy_probe:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    def step(i):
+        api.sparse_attn(qs[i], kvs[i], sink, idxs[i], w.scale, out=out, num_splits=S,
+                        workspace=ws)
+
+    # warm up eagerly (also checks that the path runs), then capture one graph per copy
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+    graphs = []
+    cap_stream = torch.cuda.Stream()
+    for i in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            step(i)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+
+    def timed(n_copies):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        gate(torch)
+        e0.record()
+        for k in range(args.steps):
+            graphs[k % n_copies].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_step = timed(R)
+    ms_step_warm = timed(1)
+
+    # the dominant kernel alone: back-to-back launches on the stream it runs on
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    gate(torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(args.steps):
+        i = k % R
+        if S > 1:
+            api.sparse_attn_partial(qs[i], kvs[i], idxs[i], w.scale, S, ws)
+        else:
+            api.sparse_attn(qs[i], kvs[i], sink, idxs[i], w.scale, out=out, num_splits=1)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_main = e0.elapsed_time(e1) / args.steps
+
+    # figures
+    Qn = w.queries
+    valid = w.valid_entries()
+    kv_bytes = w.distinct_rows() * w.D * 2
+    q_bytes = Qn * w.H * w.D * 2
+    idx_bytes = w.idxs.size * 4
+    main_bytes = kv_bytes + q_bytes + idx_bytes + (q_bytes if S == 1 else 0) + (w.H * 4 if S == 1 else 0)
+    path_bytes = w.algorithmic_bytes()
+    flops = w.algorithmic_flops()
+    t_step = ms_step * 1e-3
+    t_roof = max(path_bytes / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    achieved = main_bytes / (ms_main * 1e-3) / 1e9
+    traffic = read_counters()
+    line = {
+        "metric": "sparse-attn queries/sec + gathered-KV HBM GB/s (% roofline), H=64 D=512 K=640",
+        "value": round(Qn / t_step, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"deepseek-v4.1-{w.name}", "B": w.B, "T": w.T, "H": w.H,
+                   "D": w.D, "K": w.K, "N": w.N, "valid_entries": valid, "splits": S,
+                   "input_copies_rotated": R, "parallelism": "single-gpu"},
+        "gathered_kv_GBps": round(valid * w.D * 2 / t_step / 1e9, 1),
+        "path_roofline_frac": round(t_roof / t_step, 4),
+        "mfma_util": round(flops / t_step / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+        "warm_cache": {"value": round(Qn / (ms_step_warm * 1e-3), 1),
+                       "ms_per_step": round(ms_step_warm, 5),
+                       "note": "same inputs every step: rows may be served from the Infinity Cache"},
+        "roofline": {"kernel": "attn_fwd_kernel<512,4>", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": main_bytes,
+                     "avg_launch_us": round(ms_main * 1e3, 3)},
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        kvh = np.stack([w.kv_dense_host(b) for b in range(w.B)])
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.sparse_attn_ref(w.q, kvh, w.sink, w.idxs, w.scale)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0 or done >= 50:
+                break
+        line["cpu_baseline"] = {
+            "value": round(done * Qn / el, 2), "unit": "queries/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the full {w.name} batch ({Qn} queries) computed {done} times "
+                      f"by the fp64 oracle, {el:.1f} s wall"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,119 @@
+/*
+ * sparse_attn -- sparse latent attention with a per-head attention sink, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (DeepSeek-V4.1 pages, "Output projection" page, Attention.forward
+ * excerpt: o = sparse_attn(q, kv, attn_sink, topk_idxs, softmax_scale)):
+ *
+ *   for every query (b, t) and head h, with J = the entries of idxs[b, t, :]
+ *   that are >= 0 and < N (each occurrence counts, as a gather does):
+ *     s_j = scale * <q[b,t,h,:], kv[b,j,:]>                 for j in J
+ *     o[b,t,h,:] = sum_j exp(s_j) kv[b,j,:] / (exp(sink[h]) + sum_j exp(s_j))
+ *
+ * One latent row kv[b, j, :] is both the key and the value of position j for
+ * every head (the same excerpt joins the window rows and the compressed rows
+ * into one kv tensor and one index list).  The sink is one float32 logit per
+ * head (Attention.__init__ excerpt: attn_sink) that enlarges the denominator
+ * and carries no value; it is not multiplied by scale.  The caller passes
+ * scale (head_dim ** -0.5 in that excerpt).  With no valid entry the output is
+ * zero.  Outputs are bfloat16, rounded to nearest even from float32; scores,
+ * the running max, the denominator and the accumulators are float32, and the
+ * softmax weights enter the value product as bfloat16.
+ *
+ * Layouts (all row-major and contiguous, element strides implied by sa_dims):
+ *   q     bf16  [B, T, H, D]      (the query after unflatten to heads)
+ *   kv    bf16  [B, N, D]         (window rows first, then compressed rows)
+ *   sink  f32   [H] or NULL       (NULL = no sink)
+ *   idxs  int32 [B, T, K]         (negative = unused slot; K may be 0)
+ *   out   bf16  [B, T, H, D]      (must not overlap any input)
+ * q, kv and out must be 16-byte aligned; idxs and sink 4-byte aligned;
+ * workspace 256-byte aligned.  Supported: D in {128, 256, 512}, any H >= 1,
+ * K <= 2048.  Entries >= N are skipped by the kernels (never read); they break
+ * the caller's contract and sparse_attn_check_idxs counts them.
+ *
+ * Ownership and behaviour: the caller owns every buffer; the library never
+ * allocates or frees device memory and keeps no state beyond a once-only cache
+ * of each device's compute-unit count.  Every entry point only enqueues work
+ * on `stream` (it never synchronises or reads device memory from the host),
+ * so calls can be captured in a HIP graph.  Inputs must stay alive until the
+ * stream reaches the work.  Argument errors are reported synchronously, before
+ * any HIP call; launch failures return SA_ERR_HIP.  Nothing throws across the
+ * boundary.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+/* Sizes of one call.  B, T >= 0 (zero queries is a no-op); H, D >= 1; N >= 0; K >= 0. */
+typedef struct sa_dims {
+    int32_t B, T, H, D, N, K;
+} sa_dims;
+
+enum sa_status {
+    SA_OK = 0,
+    SA_ERR_NULL = 1,        /* a required pointer is NULL */
+    SA_ERR_SHAPE = 2,       /* a dimension is out of range */
+    SA_ERR_UNSUPPORTED = 3, /* D or K outside what the kernels are built for */
+    SA_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+    SA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than sparse_attn_workspace_bytes */
+    SA_ERR_SPLITS = 6,      /* num_splits outside [0, 64] */
+    SA_ERR_HIP = 7          /* a HIP call failed (device query or kernel launch) */
+};
+
+/* Number of index-range splits the library picks when num_splits is 0: one
+ * split when the queries alone fill the device, else enough splits (each at
+ * least 64 list entries) to give every compute unit work.  Returns >= 1, or a
+ * negative sa_status on bad dims or a failed device query. */
+int32_t sparse_attn_plan_splits(const sa_dims *d);
+
+/* Bytes of workspace sparse_attn_fwd needs for `num_splits` (0 = the planned
+ * count): 0 for one split, else float32 partial outputs [B*T, S, H, D] plus
+ * the running max and denominator [B*T, S, H] each.  Returns 0 on bad dims. */
+size_t sparse_attn_workspace_bytes(const sa_dims *d, int32_t num_splits);
+
+/* The whole step: out = sparse_attn(q, kv, sink, idxs, scale).
+ * num_splits: 0 = planned (one split when workspace is NULL), else 1..64.
+ * With more than one split the index list of each query is cut into
+ * contiguous ranges of its valid entries, each range is reduced by its own
+ * workgroup into partial (output, max, denominator) in `workspace`, and a
+ * second kernel merges the partials with the sink (log-sum-exp combine).
+ * Every split count gives the same result up to float32 rounding. */
+int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                    float scale, void *out, const sa_dims *d, int32_t num_splits,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* First half of the split path (num_splits >= 2): writes the partials of every
+ * split into `workspace` and nothing into out.  Same arguments and checks as
+ * sparse_attn_fwd, without out. */
+int sparse_attn_fwd_partial(const void *q, const void *kv, const int32_t *idxs, float scale,
+                            const sa_dims *d, int32_t num_splits, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Second half of the split path: merges the partials written by
+ * sparse_attn_fwd_partial for the same dims and num_splits with the sink and
+ * writes out. */
+int sparse_attn_fwd_combine(const float *sink, void *out, const sa_dims *d, int32_t num_splits,
+                            const void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Checked mode: adds to *d_bad_count (a device int32, zeroed by the caller)
+ * the number of entries of idxs that are >= N.  Such entries break the
+ * contract of sparse_attn_fwd (the fast path skips them). */
+int sparse_attn_check_idxs(const int32_t *idxs, const sa_dims *d, int32_t *d_bad_count,
+                           hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char *sparse_attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

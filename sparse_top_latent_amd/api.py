@@ -1,0 +1,126 @@
+"""Python binding of the sparse_attn C ABI.
+
+Argument marshalling only: dtype/shape/device checks, allocation of the output
+and workspace through torch, and the call on torch's current HIP stream.  All
+arithmetic runs in the HIP kernels of libsparse_attn.so.
+
+The argument order follows the call on the DeepSeek-V4.1 "Output projection"
+page (Attention.forward excerpt): sparse_attn(q, kv, attn_sink, topk_idxs,
+softmax_scale).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import SaDims
+
+
+def _dims(q, kv, idxs) -> SaDims:
+    if q.dim() != 4 or kv.dim() != 3 or idxs.dim() != 3:
+        raise ValueError("expected q [B,T,H,D], kv [B,N,D], idxs [B,T,K]")
+    B, T, H, D = q.shape
+    if kv.shape[0] != B or kv.shape[2] != D:
+        raise ValueError(f"kv shape {tuple(kv.shape)} does not match q {tuple(q.shape)}")
+    if idxs.shape[0] != B or idxs.shape[1] != T:
+        raise ValueError(f"idxs shape {tuple(idxs.shape)} does not match q {tuple(q.shape)}")
+    return SaDims(B, T, H, D, kv.shape[1], idxs.shape[2])
+
+
+def _check_tensors(q, kv, sink, idxs):
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
+        raise TypeError("q and kv must be bfloat16")
+    if idxs.dtype != torch.int32:
+        raise TypeError("idxs must be int32")
+    if sink is not None and (sink.dtype != torch.float32 or sink.dim() != 1
+                             or sink.shape[0] != q.shape[2]):
+        raise TypeError("sink must be float32 [H] or None")
+    for name, t in (("q", q), ("kv", kv), ("idxs", idxs), ("sink", sink)):
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be on the same GPU as q")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def plan_splits(q, kv, idxs) -> int:
+    with torch.cuda.device(q.device):
+        r = _lib.lib().sparse_attn_plan_splits(ctypes.byref(_dims(q, kv, idxs)))
+    if r < 0:
+        _lib.check(-r, "sparse_attn_plan_splits")
+    return int(r)
+
+
+def workspace_bytes(q, kv, idxs, num_splits: int = 0) -> int:
+    with torch.cuda.device(q.device):
+        return int(_lib.lib().sparse_attn_workspace_bytes(ctypes.byref(_dims(q, kv, idxs)),
+                                                          num_splits))
+
+
+def sparse_attn(q, kv, sink, idxs, scale: float, out=None, num_splits: int = 0,
+                workspace=None):
+    """o[b,t,h] = softmax over {sink_h} U {scale <q[b,t,h], kv[b,j]> : j in idxs[b,t], j >= 0}
+    applied to the rows kv[b,j] (the sink carries no value).  Returns bf16 [B,T,H,D]."""
+    _check_tensors(q, kv, sink, idxs)
+    dims = _dims(q, kv, idxs)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    L = _lib.lib()
+    with torch.cuda.device(q.device):
+        need = int(L.sparse_attn_workspace_bytes(ctypes.byref(dims), num_splits))
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = L.sparse_attn_fwd(_ptr(q), _ptr(kv), _ptr(sink), _ptr(idxs), ctypes.c_float(scale),
+                               _ptr(out), ctypes.byref(dims), num_splits, _ptr(workspace),
+                               ws_bytes, _stream(q.device))
+    _lib.check(rc, "sparse_attn_fwd")
+    return out
+
+
+def sparse_attn_partial(q, kv, idxs, scale: float, num_splits: int, workspace):
+    """First kernel of the split path: per-split partials into ``workspace``."""
+    _check_tensors(q, kv, None, idxs)
+    dims = _dims(q, kv, idxs)
+    with torch.cuda.device(q.device):
+        rc = _lib.lib().sparse_attn_fwd_partial(
+            _ptr(q), _ptr(kv), _ptr(idxs), ctypes.c_float(scale), ctypes.byref(dims),
+            num_splits, _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(q.device))
+    _lib.check(rc, "sparse_attn_fwd_partial")
+
+
+def sparse_attn_combine(q_shape, N: int, K: int, sink, out, num_splits: int, workspace):
+    """Second kernel of the split path: merge the partials with the sink into ``out``."""
+    B, T, H, D = q_shape
+    dims = SaDims(B, T, H, D, N, K)
+    with torch.cuda.device(out.device):
+        rc = _lib.lib().sparse_attn_fwd_combine(
+            _ptr(sink), _ptr(out), ctypes.byref(dims), num_splits, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(out.device))
+    _lib.check(rc, "sparse_attn_fwd_combine")
+
+
+def check_idxs(idxs, N: int) -> int:
+    """Number of entries >= N (checked mode); synchronises to read the count."""
+    B, T, K = idxs.shape
+    dims = SaDims(B, T, 1, 128, N, K)
+    bad = torch.zeros(1, dtype=torch.int32, device=idxs.device)
+    with torch.cuda.device(idxs.device):
+        rc = _lib.lib().sparse_attn_check_idxs(_ptr(idxs), ctypes.byref(dims), _ptr(bad),
+                                                _stream(idxs.device))
+    _lib.check(rc, "sparse_attn_check_idxs")
+    return int(bad.item())

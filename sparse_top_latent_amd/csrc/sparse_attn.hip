@@ -1,0 +1,618 @@
+// Sparse latent attention with a per-head sink for gfx950 (MI355X).
+//
+// Operation: DeepSeek-V4.1 pages, "Output projection" page, Attention.forward
+// excerpt (o = sparse_attn(q, kv, attn_sink, topk_idxs, softmax_scale)); the
+// semantics and layouts are stated in include/sparse_attn.h.
+//
+// Kernels
+//   attn_fwd    one workgroup per (query, head group, split).  Steps:
+//               index decode + compaction of the query's list into LDS, a
+//               per-split slice of the valid entries, then chunks of 32 rows:
+//               LDS-DMA gather of the rows (16 B per lane, double buffered),
+//               S^T = K Q^T on 16x16x32 bf16 MFMAs, the online sink-softmax in
+//               float32, O^T += V^T P^T on MFMAs with V read through LDS
+//               transpose loads.  Epilogue: bf16 output, or float32 partials.
+//   combine     log-sum-exp merge of split partials plus the sink -> bf16.
+//   check_idxs  counts entries >= N.
+//
+// Work split inside a workgroup: wave w owns 16 heads for both products, so
+// the softmax of a head never leaves its wave; the four waves share one LDS
+// copy of each row chunk (one HBM read per row per workgroup).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "sparse_attn.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int KC = 32;                // rows (list entries) per chunk
+constexpr int LIST_CAP = 2048;        // longest index list a workgroup compacts
+constexpr int MAX_SPLITS = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+// The running max is only raised when a chunk beats it by more than this many
+// log2 units; until then weights stay <= 2^8 relative to the kept max, which
+// float32 sums and bf16 weights hold without loss, and the output (numerator
+// and denominator share the reference) is unchanged.
+constexpr float MAX_SLACK = 8.0f;
+
+struct FwdParams {
+    const uint16_t *q;
+    const uint16_t *kv;
+    const float *sink;
+    const int32_t *idxs;
+    uint16_t *out;     // non-split path
+    float *ws_o;       // split path: [Q, S, H, D]
+    float *ws_m;       // [Q, S, H] running max, log2 units
+    float *ws_l;       // [Q, S, H] denominator relative to ws_m
+    int64_t N;
+    int32_t T, H, K;
+    int32_t S, HG, units, per_xcd;
+    float qk_scale_log2;  // scale * log2(e)
+};
+
+// Row swizzle of the 16-byte chunks inside a row of the LDS tile: chunk c of
+// row r lives at position c ^ swz(r).  Rows are 2*D bytes apart (a multiple
+// of 256 B, so every row starts on the same bank); the XOR spreads the 16
+// rows read by a b128 MFMA-operand load, and the 4x2 chunks read by each
+// 16-lane block of a transpose load, over distinct banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to two bf16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// Compacts the valid entries (0 <= idx < N) of one list into `list`, keeping
+// their order, and returns how many there are.  All threads take part.
+template <int NT>
+__device__ int compact_list(const int32_t *__restrict__ lst, int K, int64_t N, int32_t *list,
+                            int32_t *wave_cnt) {
+    constexpr int NWV = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    int base = 0;
+    for (int k0 = 0; k0 < K; k0 += NT) {
+        const int k = k0 + tid;
+        const int v = k < K ? lst[k] : -1;
+        const bool ok = v >= 0 && (int64_t)v < N;
+        const uint64_t mask = __ballot(ok);
+        const int before = __popcll(mask & ((1ull << lane) - 1ull));
+        if (lane == 0) wave_cnt[wid] = __popcll(mask);
+        __syncthreads();
+        int off = base, total = 0;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+            const int c = wave_cnt[w];
+            off += w < wid ? c : 0;
+            total += c;
+        }
+        if (ok) list[off + before] = v;
+        base += total;
+        __syncthreads();
+    }
+    return base;
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
+    constexpr int NT = NW * 64;
+    constexpr int ROWB = D * 2;            // bytes per row
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;          // rows per LDS-DMA wave instruction
+    constexpr int NINS = KC / RPI;         // DMA wave instructions per chunk
+    constexpr int DS = D / 32;             // MFMA k-steps over d
+    constexpr int DT = D / 16;             // 16-wide d tiles of the output
+    static_assert(CPR >= 16 && 64 % CPR == 0, "row swizzle needs D in {128, 256, 512}");
+
+    __shared__ __attribute__((aligned(16))) uint8_t tile[2][KC * ROWB];
+    __shared__ int32_t list[LIST_CAP];
+    __shared__ int32_t wave_cnt[NW];
+
+    // XCD-aware unit order: consecutive units (the splits and head groups of
+    // one query, or neighbouring queries) run on the same XCD and share its L2.
+    const int bid = blockIdx.x;
+    const int unit = (bid & 7) * p.per_xcd + (bid >> 3);
+    if (unit >= p.units) return;
+    const int s = unit % p.S;
+    const int hg = (unit / p.S) % p.HG;
+    const int qi = unit / (p.S * p.HG);
+    const int b = qi / p.T;
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int g = lane >> 4;      // 16-lane block of the wave
+    const int li = lane & 15;
+
+    // a1: decode and compact the list, then take this split's slice.
+    const int n = compact_list<NT>(p.idxs + (int64_t)qi * p.K, p.K, p.N, list, wave_cnt);
+    const int lo = (int)(((int64_t)n * s) / p.S);
+    const int hi = (int)(((int64_t)n * (s + 1)) / p.S);
+    const int nchunks = (hi - lo + KC - 1) / KC;
+
+    // a3: this lane's head and its query row, held as MFMA B operands:
+    // qf[k] = q[h, 32k + 8g .. 32k + 8g + 7].
+    const int h = hg * (NW * 16) + wid * 16 + li;
+    const bool h_ok = h < p.H;
+    bf16x8_t qf[DS];
+    {
+        const uint16_t *qrow = p.q + ((int64_t)qi * p.H + (h_ok ? h : 0)) * D;
+#pragma unroll
+        for (int k = 0; k < DS; ++k) {
+            u32x4_t v = *(const u32x4_t *)(qrow + 32 * k + 8 * g);
+            if (!h_ok) v = u32x4_t{0, 0, 0, 0};
+            qf[k] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+
+    // Softmax state of head h (log2 units).  The non-split path starts from
+    // the sink: max = sink, denominator = 1 (counted once, in block 0).
+    float m = -INFINITY, lsum = 0.f;
+    if (p.S == 1 && p.sink != nullptr && h_ok) {
+        m = p.sink[h] * LOG2E;
+        lsum = g == 0 ? 1.f : 0.f;
+    }
+    f32x4_t o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const uint16_t *kvb = p.kv + (int64_t)b * p.N * D;
+
+    // a2: gather the rows of chunk c into LDS buffer `buf` with LDS-DMA.
+    // Each wave instruction moves RPI whole rows: lane l lands at byte 16*l of
+    // the instruction's 1 KB, i.e. row r = l / CPR at position l % CPR, so it
+    // fetches the row's chunk (position ^ swz(r)).  Tail slots repeat the
+    // chunk's first row; their scores are masked to -inf below.
+    auto stage = [&](int c, int buf) {
+        const int e0 = lo + c * KC;
+        static_assert(NINS % NW == 0, "DMA instructions must split evenly over the waves");
+#pragma unroll
+        for (int k = 0; k < NINS / NW; ++k) {
+            const int ii = k * NW + wid;
+            const int r = ii * RPI + lane / CPR;
+            const int pos = lane % CPR;
+            const int e = e0 + r;
+            const int row = list[e < hi ? e : e0];
+            const uint16_t *src = kvb + (int64_t)row * D + ((pos ^ swz(r)) << 3);
+            LDS_AS void *dst = (LDS_AS void *)((LDS_AS uint8_t *)&tile[buf][0] + ii * 1024);
+            __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+        }
+    };
+
+    if (nchunks > 0) stage(0, 0);
+
+    for (int c = 0; c < nchunks; ++c) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (c + 1 < nchunks) stage(c + 1, (c + 1) & 1);
+
+        const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c & 1][0];
+        const int cnt = min(KC, hi - (lo + c * KC));
+
+        // a4: S^T[j, h] for j in the chunk (two 16-row tiles).
+        f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int k = 0; k < DS; ++k) {
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                const int r = jt * 16 + li;
+                const int pos = (4 * k + g) ^ swz(r);
+                const u32x4_t a = *(const LDS_AS u32x4_t *)(T + r * ROWB + pos * 16);
+                sacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, a), qf[k], sacc[jt], 0, 0, 0);
+            }
+        }
+
+        // a5: mask + online sink-softmax.  Lane (li, g) holds rows
+        // j = 16 jt + 4 g + i of head h.
+        float sv[8];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 16 * jt + 4 * g + i;
+                const float x = j < cnt ? sacc[jt][i] * p.qk_scale_log2 : -INFINITY;
+                sv[jt * 4 + i] = x;
+                cmax = fmaxf(cmax, x);
+            }
+        cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
+        cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+        const bool raise = cmax > m + MAX_SLACK;
+        if (__ballot(raise)) {
+            const float mnew = raise ? cmax : m;
+            const float alpha = exp2_fast(m - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) o[t] *= alpha;
+            m = mnew;
+        }
+        // The weights enter the value product as bf16; the denominator sums
+        // the same rounded weights, so numerator and denominator agree.
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(sv[e] - m);
+        const u32x4_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3]),
+                            pack2_bf16(pv[4], pv[5]), pack2_bf16(pv[6], pv[7])};
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            psum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
+        lsum += psum;
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+
+        // a6: O^T[d, h] += V^T[d, j] P^T[j, h].  A operand through transpose
+        // loads: lane i of block g addresses row 4g + i/4 (and +16), columns
+        // 16t + 4(i%4) .. +3; the load hands lane i column 16t + i of rows
+        // 4g..4g+3, matching the weight slots j = 4g + e and 16 + 4g + e.
+        {
+            const int r0 = 4 * g + (li >> 2);
+            const int sw = swz(r0);  // rows r0 and r0 + 16 share the swizzle
+            const int half = (li & 1) * 8;
+            const LDS_AS uint8_t *R0 = T + r0 * ROWB + half;
+            const LDS_AS uint8_t *R1 = R0 + 16 * ROWB;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const int pos = ((2 * t + ((li >> 1) & 1)) ^ sw) * 16;
+                const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R0 + pos));
+                const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R1 + pos));
+                const bf16x8_t a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[t], 0, 0, 0);
+            }
+        }
+    }
+
+    // a7 / a8: epilogue.  Lane (li, g) holds O^T[16t + 4g + i, h].
+    float ltot = lsum + shfl_xor_f(lsum, 16);
+    ltot += shfl_xor_f(ltot, 32);
+    if (!h_ok) return;
+    if (p.S == 1) {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        uint16_t *orow = p.out + ((int64_t)qi * p.H + h) * D + 4 * g;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const u32x2_t w = {pack2_bf16(o[t][0] * inv, o[t][1] * inv),
+                               pack2_bf16(o[t][2] * inv, o[t][3] * inv)};
+            *(u32x2_t *)(orow + 16 * t) = w;
+        }
+    } else {
+        const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
+        float *orow = p.ws_o + slot * D + 4 * g;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) *(f32x4_t *)(orow + 16 * t) = o[t];
+        if (g == 0) {
+            p.ws_m[slot] = m;
+            p.ws_l[slot] = ltot;
+        }
+    }
+}
+
+// a9: out[q, h, :] = (sum_s 2^(m_s - M) O_s + 0) / (2^(sink - M) + sum_s 2^(m_s - M) l_s),
+// M = max(sink, max_s m_s), all in log2 units.  One thread per 4 outputs.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ws_o,
+                                                      const float *__restrict__ ws_m,
+                                                      const float *__restrict__ ws_l,
+                                                      const float *__restrict__ sink,
+                                                      uint16_t *__restrict__ out, int64_t QH,
+                                                      int H, int S) {
+    constexpr int DQ = D / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= QH * DQ) return;
+    const int64_t qh = idx / DQ;
+    const int dq = (int)(idx % DQ);
+    const int64_t qi = qh / H;
+    const int h = (int)(qh % H);
+    const float mz = sink != nullptr ? sink[h] * LOG2E : -INFINITY;
+    float mx = mz;
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, ws_m[(qi * S + s) * H + h]);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    if (mx != -INFINITY) {
+        L = sink != nullptr ? exp2_fast(mz - mx) : 0.f;
+        for (int s = 0; s < S; ++s) {
+            const int64_t slot = (qi * S + s) * H + h;
+            const float w = exp2_fast(ws_m[slot] - mx);
+            L += w * ws_l[slot];
+            acc += w * *(const f32x4_t *)(ws_o + slot * D + 4 * dq);
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const u32x2_t w = {pack2_bf16(acc[0] * inv, acc[1] * inv), pack2_bf16(acc[2] * inv, acc[3] * inv)};
+    *(u32x2_t *)(out + qh * D + 4 * dq) = w;
+}
+
+__global__ __launch_bounds__(256) void check_idxs_kernel(const int32_t *__restrict__ idxs,
+                                                         int64_t total, int64_t N,
+                                                         int32_t *bad) {
+    int cnt = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256)
+        cnt += (int64_t)idxs[i] >= N ? 1 : 0;
+    // wave reduction, then one vector atomic per wave
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(bad, cnt);
+}
+
+// ------------------------------------------------------------------ host side
+
+int device_cu_count() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            return -1;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+int waves_for(int H) { return H >= 64 ? 4 : H > 16 ? (H > 32 ? 4 : 2) : 1; }
+
+int check_dims(const sa_dims *d) {
+    if (d == nullptr) return SA_ERR_NULL;
+    if (d->B < 0 || d->T < 0 || d->H < 1 || d->D < 1 || d->N < 0 || d->K < 0) return SA_ERR_SHAPE;
+    if (d->D != 128 && d->D != 256 && d->D != 512) return SA_ERR_UNSUPPORTED;
+    if (d->K > LIST_CAP) return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
+bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+int64_t queries(const sa_dims *d) { return (int64_t)d->B * d->T; }
+
+struct WsLayout {
+    size_t o_off, m_off, l_off, bytes;
+};
+
+WsLayout ws_layout(const sa_dims *d, int S) {
+    WsLayout w{0, 0, 0, 0};
+    if (S <= 1) return w;
+    const size_t slots = (size_t)queries(d) * S * d->H;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    w.o_off = 0;
+    w.m_off = up(slots * d->D * sizeof(float));
+    w.l_off = w.m_off + up(slots * sizeof(float));
+    w.bytes = w.l_off + up(slots * sizeof(float));
+    return w;
+}
+
+int plan_splits(const sa_dims *d) {
+    const int cus = device_cu_count();
+    if (cus < 0) return -SA_ERR_HIP;
+    const int nw = waves_for(d->H);
+    const int64_t hg = (d->H + 16 * nw - 1) / (16 * nw);
+    const int64_t units = queries(d) * hg;
+    if (units <= 0 || units >= cus) return 1;
+    int64_t S = (cus + units - 1) / units;
+    const int64_t max_by_len = d->K / 64 > 1 ? d->K / 64 : 1;
+    if (S > max_by_len) S = max_by_len;
+    if (S > MAX_SPLITS) S = MAX_SPLITS;
+    return (int)(S < 1 ? 1 : S);
+}
+
+template <int D, int NW>
+hipError_t launch_fwd(const FwdParams &p, hipStream_t stream) {
+    const int grid = 8 * p.per_xcd;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW>), dim3(grid), dim3(NW * 64), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fwd_d(int nw, const FwdParams &p, hipStream_t stream) {
+    switch (nw) {
+        case 1: return launch_fwd<D, 1>(p, stream);
+        case 2: return launch_fwd<D, 2>(p, stream);
+        default: return launch_fwd<D, 4>(p, stream);
+    }
+}
+
+hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
+                          const void *ws, const WsLayout &L, hipStream_t stream) {
+    const int64_t QH = queries(d) * d->H;
+    const int64_t threads = QH * (d->D / 4);
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    const float *wo = (const float *)((const uint8_t *)ws + L.o_off);
+    const float *wm = (const float *)((const uint8_t *)ws + L.m_off);
+    const float *wl = (const float *)((const uint8_t *)ws + L.l_off);
+    uint16_t *o = (uint16_t *)out;
+    switch (d->D) {
+        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, sink, o, QH, d->H, S); break;
+        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, sink, o, QH, d->H, S); break;
+        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, sink, o, QH, d->H, S); break;
+    }
+    return hipGetLastError();
+}
+
+// Argument checks shared by the entry points; resolves the split count.
+int check_common(const void *q, const void *kv, const int32_t *idxs, const sa_dims *d,
+                 int32_t num_splits, void *ws, size_t ws_bytes, bool need_ws, int *S_out) {
+    int rc = check_dims(d);
+    if (rc != SA_OK) return rc;
+    if (num_splits < 0 || num_splits > MAX_SPLITS) return SA_ERR_SPLITS;
+    if (queries(d) == 0) {
+        *S_out = num_splits > 0 ? num_splits : 1;
+        return SA_OK;
+    }
+    if (q == nullptr || kv == nullptr || (idxs == nullptr && d->K > 0)) return SA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(idxs, 4)) return SA_ERR_ALIGN;
+    int S = num_splits;
+    if (S == 0) {
+        if (ws == nullptr && !need_ws) {
+            S = 1;
+        } else {
+            S = plan_splits(d);
+            if (S < 0) return -S;
+        }
+    }
+    if (need_ws && S < 2) return SA_ERR_SPLITS;
+    if (S > 1) {
+        if (ws == nullptr) return SA_ERR_WORKSPACE;
+        if (!aligned(ws, 256)) return SA_ERR_ALIGN;
+        if (ws_bytes < ws_layout(d, S).bytes) return SA_ERR_WORKSPACE;
+    }
+    *S_out = S;
+    return SA_OK;
+}
+
+FwdParams make_params(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                      float scale, void *out, const sa_dims *d, int S, void *ws) {
+    FwdParams p{};
+    p.q = (const uint16_t *)q;
+    p.kv = (const uint16_t *)kv;
+    p.sink = sink;
+    p.idxs = idxs;
+    p.out = (uint16_t *)out;
+    const WsLayout L = ws_layout(d, S);
+    if (S > 1) {
+        p.ws_o = (float *)((uint8_t *)ws + L.o_off);
+        p.ws_m = (float *)((uint8_t *)ws + L.m_off);
+        p.ws_l = (float *)((uint8_t *)ws + L.l_off);
+    }
+    p.N = d->N;
+    p.T = d->T;
+    p.H = d->H;
+    p.K = d->K;
+    p.S = S;
+    const int nw = waves_for(d->H);
+    p.HG = (d->H + 16 * nw - 1) / (16 * nw);
+    const int64_t units = queries(d) * p.HG * S;
+    p.units = (int32_t)units;
+    p.per_xcd = (int32_t)((units + 7) / 8);
+    p.qk_scale_log2 = scale * LOG2E;
+    return p;
+}
+
+hipError_t run_fwd(const FwdParams &p, int D, int H, hipStream_t stream) {
+    const int nw = waves_for(H);
+    switch (D) {
+        case 128: return launch_fwd_d<128>(nw, p, stream);
+        case 256: return launch_fwd_d<256>(nw, p, stream);
+        default: return launch_fwd_d<512>(nw, p, stream);
+    }
+}
+
+bool units_fit(const sa_dims *d, int S) {
+    const int nw = waves_for(d->H);
+    const int64_t hg = (d->H + 16 * nw - 1) / (16 * nw);
+    return queries(d) * hg * S <= (int64_t)0x7FFFFFF0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sparse_attn_plan_splits(const sa_dims *d) {
+    const int rc = check_dims(d);
+    if (rc != SA_OK) return -rc;
+    return plan_splits(d);
+}
+
+size_t sparse_attn_workspace_bytes(const sa_dims *d, int32_t num_splits) {
+    if (check_dims(d) != SA_OK || num_splits < 0 || num_splits > MAX_SPLITS) return 0;
+    int S = num_splits;
+    if (S == 0) {
+        S = plan_splits(d);
+        if (S < 0) return 0;
+    }
+    return ws_layout(d, S).bytes;
+}
+
+int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                    float scale, void *out, const sa_dims *d, int32_t num_splits, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+    int S = 1;
+    int rc = check_common(q, kv, idxs, d, num_splits, workspace, workspace_bytes, false, &S);
+    if (rc != SA_OK) return rc;
+    if (queries(d) == 0) return SA_OK;
+    if (out == nullptr) return SA_ERR_NULL;
+    if (!aligned(out, 16) || !aligned(sink, 4)) return SA_ERR_ALIGN;
+    if (!units_fit(d, S)) return SA_ERR_SHAPE;
+    const FwdParams p = make_params(q, kv, sink, idxs, scale, out, d, S, workspace);
+    if (run_fwd(p, d->D, d->H, stream) != hipSuccess) return SA_ERR_HIP;
+    if (S > 1 && launch_combine(d, S, sink, out, workspace, ws_layout(d, S), stream) != hipSuccess)
+        return SA_ERR_HIP;
+    return SA_OK;
+}
+
+int sparse_attn_fwd_partial(const void *q, const void *kv, const int32_t *idxs, float scale,
+                            const sa_dims *d, int32_t num_splits, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    int S = 1;
+    int rc = check_common(q, kv, idxs, d, num_splits, workspace, workspace_bytes, true, &S);
+    if (rc != SA_OK) return rc;
+    if (queries(d) == 0) return SA_OK;
+    if (!units_fit(d, S)) return SA_ERR_SHAPE;
+    const FwdParams p = make_params(q, kv, nullptr, idxs, scale, nullptr, d, S, workspace);
+    return run_fwd(p, d->D, d->H, stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+int sparse_attn_fwd_combine(const float *sink, void *out, const sa_dims *d, int32_t num_splits,
+                            const void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_dims(d);
+    if (rc != SA_OK) return rc;
+    if (num_splits < 2 || num_splits > MAX_SPLITS) return SA_ERR_SPLITS;
+    if (queries(d) == 0) return SA_OK;
+    if (out == nullptr) return SA_ERR_NULL;
+    if (workspace == nullptr) return SA_ERR_WORKSPACE;
+    if (!aligned(out, 16) || !aligned(sink, 4) || !aligned(workspace, 256)) return SA_ERR_ALIGN;
+    const WsLayout L = ws_layout(d, num_splits);
+    if (workspace_bytes < L.bytes) return SA_ERR_WORKSPACE;
+    return launch_combine(d, num_splits, sink, out, workspace, L, stream) == hipSuccess
+               ? SA_OK
+               : SA_ERR_HIP;
+}
+
+int sparse_attn_check_idxs(const int32_t *idxs, const sa_dims *d, int32_t *d_bad_count,
+                           hipStream_t stream) {
+    if (d == nullptr) return SA_ERR_NULL;
+    if (d->B < 0 || d->T < 0 || d->N < 0 || d->K < 0) return SA_ERR_SHAPE;
+    const int64_t total = queries(d) * d->K;
+    if (total == 0) return SA_OK;
+    if (idxs == nullptr || d_bad_count == nullptr) return SA_ERR_NULL;
+    if (!aligned(idxs, 4) || !aligned(d_bad_count, 4)) return SA_ERR_ALIGN;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(check_idxs_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, idxs, total,
+                       (int64_t)d->N, d_bad_count);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+const char *sparse_attn_status_str(int status) {
+    switch (status) {
+        case SA_OK: return "ok";
+        case SA_ERR_NULL: return "a required pointer is NULL";
+        case SA_ERR_SHAPE: return "a dimension is out of range";
+        case SA_ERR_UNSUPPORTED: return "unsupported size (D must be 128, 256 or 512; K <= 2048)";
+        case SA_ERR_ALIGN: return "misaligned pointer (q/kv/out 16 B, idxs/sink 4 B, workspace 256 B)";
+        case SA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SA_ERR_SPLITS: return "num_splits out of range";
+        case SA_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

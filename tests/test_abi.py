@@ -1,0 +1,133 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and rejects bad arguments before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_top_latent_amd import _lib
+from sparse_top_latent_amd._lib import SaDims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN, SA_ERR_WORKSPACE, \
+    SA_ERR_SPLITS, SA_ERR_HIP = range(8)
+
+# fake device addresses: never dereferenced, because every call below fails its
+# argument checks first
+A = ctypes.c_void_p(0x10000)
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10002)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sparse_attn_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 7
+    assert set(names) == set(_lib.SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def dims(B=2, T=3, H=64, D=512, N=100, K=40):
+    return ctypes.byref(SaDims(B, T, H, D, N, K))
+
+
+def fwd(L, q=A, kv=A, sink=None, idxs=A, out=A2, d=None, S=1, ws=None, wsb=0):
+    return L.sparse_attn_fwd(q, kv, sink, idxs, ctypes.c_float(0.1), out,
+                             dims() if d is None else d, S, ws, wsb, None)
+
+
+def test_status_strings(L):
+    seen = set()
+    for rc in range(8):
+        s = _lib.status_str(rc)
+        assert s and s not in seen
+        seen.add(s)
+    assert _lib.status_str(99) == "unknown status"
+
+
+def test_dims_errors(L):
+    assert fwd(L, d=ctypes.POINTER(SaDims)()) == SA_ERR_NULL
+    assert fwd(L, d=dims(H=0)) == SA_ERR_SHAPE
+    assert fwd(L, d=dims(D=0)) == SA_ERR_SHAPE
+    assert fwd(L, d=dims(B=-1)) == SA_ERR_SHAPE
+    assert fwd(L, d=dims(K=-1)) == SA_ERR_SHAPE
+    assert fwd(L, d=dims(N=-5)) == SA_ERR_SHAPE
+    assert fwd(L, d=dims(D=64)) == SA_ERR_UNSUPPORTED
+    assert fwd(L, d=dims(D=100)) == SA_ERR_UNSUPPORTED
+    assert fwd(L, d=dims(K=2049)) == SA_ERR_UNSUPPORTED
+
+
+def test_pointer_errors(L):
+    assert fwd(L, q=None) == SA_ERR_NULL
+    assert fwd(L, kv=None) == SA_ERR_NULL
+    assert fwd(L, idxs=None) == SA_ERR_NULL
+    assert fwd(L, out=None) == SA_ERR_NULL
+    assert fwd(L, q=MIS) == SA_ERR_ALIGN
+    assert fwd(L, kv=MIS) == SA_ERR_ALIGN
+    assert fwd(L, out=MIS) == SA_ERR_ALIGN
+    assert fwd(L, idxs=ctypes.c_void_p(0x10001)) == SA_ERR_ALIGN
+    assert fwd(L, sink=ctypes.c_void_p(0x10002)) == SA_ERR_ALIGN
+
+
+def test_split_and_workspace_errors(L):
+    assert fwd(L, S=-1) == SA_ERR_SPLITS
+    assert fwd(L, S=65) == SA_ERR_SPLITS
+    assert fwd(L, S=2) == SA_ERR_WORKSPACE                      # no workspace
+    assert fwd(L, S=2, ws=A, wsb=16) == SA_ERR_WORKSPACE        # too small
+    assert fwd(L, S=2, ws=ctypes.c_void_p(0x10010), wsb=1 << 30) == SA_ERR_ALIGN
+    d = dims()
+    assert L.sparse_attn_fwd_partial(A, A, A, ctypes.c_float(1.0), d, 1, A, 1 << 30,
+                                     None) == SA_ERR_SPLITS
+    assert L.sparse_attn_fwd_combine(None, A, d, 1, A, 1 << 30, None) == SA_ERR_SPLITS
+    assert L.sparse_attn_fwd_combine(None, A, d, 2, None, 1 << 30, None) == SA_ERR_WORKSPACE
+    assert L.sparse_attn_fwd_combine(None, A, d, 2, A, 16, None) == SA_ERR_WORKSPACE
+    assert L.sparse_attn_fwd_combine(None, None, d, 2, A, 1 << 30, None) == SA_ERR_NULL
+
+
+def test_zero_queries_is_a_noop(L):
+    assert fwd(L, q=None, kv=None, idxs=None, out=None, d=dims(B=0)) == SA_OK
+    assert fwd(L, q=None, kv=None, idxs=None, out=None, d=dims(T=0)) == SA_OK
+
+
+def test_workspace_size_formula(L):
+    B, T, H, D, S = 3, 5, 64, 512, 4
+    got = L.sparse_attn_workspace_bytes(dims(B=B, T=T, H=H, D=D), S)
+    up = lambda x: (x + 255) // 256 * 256
+    slots = B * T * S * H
+    assert got == up(slots * D * 4) + 2 * up(slots * 4)
+    assert L.sparse_attn_workspace_bytes(dims(), 1) == 0
+    assert L.sparse_attn_workspace_bytes(dims(D=100), 2) == 0
+
+
+def test_check_idxs_errors(L):
+    assert L.sparse_attn_check_idxs(A, ctypes.POINTER(SaDims)(), A2, None) == SA_ERR_NULL
+    assert L.sparse_attn_check_idxs(None, dims(), A2, None) == SA_ERR_NULL
+    assert L.sparse_attn_check_idxs(A, dims(), None, None) == SA_ERR_NULL
+    assert L.sparse_attn_check_idxs(A, dims(), ctypes.c_void_p(0x10001), None) == SA_ERR_ALIGN
+    assert L.sparse_attn_check_idxs(None, dims(K=0), None, None) == SA_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from sparse_top_latent_amd import sparse_attn
+    q = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 4, 128, dtype=torch.bfloat16)
+    idx = torch.zeros(1, 1, 2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sparse_attn(q, kv, None, idx, 0.1)
+    with pytest.raises(TypeError):
+        sparse_attn(q.float(), kv, None, idx, 0.1)

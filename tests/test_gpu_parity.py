@@ -1,0 +1,226 @@
+"""HIP path against the fp64 oracle on the same seeded inputs (needs the GPU).
+
+Bar (floating point): max-abs error <= 1e-2 and mean-abs error <= 1e-3 over
+every compared output element, on inputs ~N(0,1).  The oracle is fp64; the GPU
+path rounds the output to bf16 and feeds the softmax weights to the MFMA in
+bf16, which keeps the expected error near 1e-4.
+"""
+import numpy as np
+import pytest
+
+from sparse_top_latent_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+
+
+def torch_mod():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def to_dev(w, idxs=None, sink=True, q_bits=None):
+    torch = torch_mod()
+    q = torch.from_numpy((w.q if q_bits is None else q_bits).view(np.int16)).cuda()
+    q = q.view(torch.bfloat16)
+    kv = w.kv_device("cuda")
+    idx = torch.from_numpy(np.ascontiguousarray(w.idxs if idxs is None else idxs)).cuda()
+    sk = torch.from_numpy(w.sink).cuda() if sink is True else (
+        None if sink is None or sink is False else torch.from_numpy(np.asarray(sink, np.float32)).cuda())
+    return q, kv, sk, idx
+
+
+def run_gpu(w, num_splits=0, idxs=None, sink=True, q_bits=None):
+    torch = torch_mod()
+    from sparse_top_latent_amd import sparse_attn
+    q, kv, sk, idx = to_dev(w, idxs, sink, q_bits)
+    out = sparse_attn(q, kv, sk, idx, w.scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    return wl.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def sink_of(w, sink):
+    if sink is True:
+        return w.sink
+    if sink is None or sink is False:
+        return None
+    return np.asarray(sink, np.float32)
+
+
+def assert_close(got, exp, what=""):
+    """max |err| / max(1, |exp|) <= 1e-2 and mean |err| <= 1e-3.
+
+    On the configured workloads |exp| < 1 everywhere, so this is exactly the
+    absolute bar.  Edge cases whose outputs exceed 1 in magnitude (one valid
+    row, a huge query) get the bar relative to |exp|: a bf16 output holds 8
+    significant bits, so its own rounding is up to 2^-9 |exp|."""
+    assert got.shape == exp.shape
+    assert np.isfinite(got).all(), f"{what}: non-finite GPU output"
+    err = np.abs(got - exp)
+    rel = err / np.maximum(1.0, np.abs(exp))
+    mx = float(rel.max()) if err.size else 0.0
+    mean = float(err.mean()) if err.size else 0.0
+    print(f"{what}: max_abs={float(err.max()) if err.size else 0.0:.3e} "
+          f"max_scaled={mx:.3e} mean_abs={mean:.3e}", flush=True)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{what}: max {mx:.3e} mean {mean:.3e}"
+
+
+def check(ref, w, num_splits=0, idxs=None, sink=True, q_bits=None, what=""):
+    lst = w.idxs if idxs is None else idxs
+    got = run_gpu(w, num_splits, lst, sink, q_bits)
+    exp = ref(w.q if q_bits is None else q_bits, w.kv_host(), sink_of(w, sink), lst, w.scale)
+    assert_close(got, exp, what or f"{w.name} S={num_splits}")
+    return got
+
+
+# ------------------------------------------------------------------ small cases
+
+@pytest.mark.parametrize("S", [0, 1, 2, 3])
+@pytest.mark.parametrize("sink", [True, None])
+def test_tiny(ref, S, sink):
+    check(ref, wl.make_tiny(), S, sink=sink, what=f"tiny S={S} sink={sink is not None}")
+
+
+@pytest.mark.parametrize("H,D", [(8, 128), (16, 256), (32, 512), (48, 512), (64, 512),
+                                 (64, 128), (64, 256), (1, 128)])
+@pytest.mark.parametrize("S", [1, 3])
+def test_shapes_span_tiles_and_tail(ref, H, D, S):
+    # K=173 with ~30% unused: several 32-row chunks and a ragged tail per split
+    w = wl.make_random(100 + H + D, 2, 2, H, D, 300, 173, p_unused=0.3)
+    check(ref, w, S, what=f"H={H} D={D} S={S}")
+
+
+def test_empty_and_all_unused(ref):
+    w = wl.make_random(7, 2, 3, 64, 512, 50, 8, p_unused=0.0)
+    for S in (0, 1, 2):
+        for sink in (True, None):
+            got = run_gpu(w, S, np.full((2, 3, 8), -1, np.int32), sink)
+            assert np.all(got == 0)
+            got0 = run_gpu(w, S, np.zeros((2, 3, 0), np.int32), sink)
+            assert got0.shape == (2, 3, 64, 512) and np.all(got0 == 0)
+
+
+def test_single_entry_and_short_lists(ref):
+    w = wl.make_random(8, 2, 2, 64, 512, 700, 641, p_unused=0.0)
+    for K in (1, 24, 33, 641):
+        lst = np.ascontiguousarray(w.idxs[..., :K])
+        check(ref, w, 0, idxs=lst, what=f"K={K}")
+
+
+@pytest.mark.parametrize("sinkval", [30.0, -30.0])
+def test_extreme_sinks(ref, sinkval):
+    w = wl.make_random(9, 2, 2, 64, 512, 200, 150, p_unused=0.2)
+    for S in (1, 2):
+        check(ref, w, S, sink=np.full(64, sinkval), what=f"sink={sinkval} S={S}")
+
+
+def test_large_norm_queries(ref):
+    w = wl.make_random(10, 2, 2, 64, 512, 200, 150, p_unused=0.2)
+    q8 = wl.to_bf16_bits(wl.bf16_bits_to_f32(w.q) * 8.0)  # scores ~8x: stresses max rescaling
+    for S in (1, 3):
+        check(ref, w, S, q_bits=q8, what=f"8x query S={S}")
+
+
+def test_permuted_lists_and_scattered_unused(ref):
+    w = wl.make_random(11, 2, 2, 64, 512, 400, 300, p_unused=0.3)
+    rng = np.random.default_rng(0)
+    perm = w.idxs.copy()
+    for b in range(2):
+        for t in range(2):
+            perm[b, t] = perm[b, t][rng.permutation(300)]
+    a = check(ref, w, 0, what="unpermuted")
+    b = check(ref, w, 0, idxs=perm, what="permuted")
+    assert np.abs(a - b).max() <= 2 * MAX_ABS
+
+
+def test_repeated_indices_count_per_occurrence(ref):
+    w = wl.make_random(12, 1, 2, 64, 512, 20, 64, allow_repeats=True, p_unused=0.1)
+    check(ref, w, 0, what="repeats")
+    check(ref, w, 2, what="repeats S=2")
+
+
+def test_entries_beyond_n_are_skipped(ref):
+    w = wl.make_random(13, 2, 2, 64, 512, 200, 100, p_unused=0.1)
+    bad = w.idxs.copy()
+    bad[0, 0, 5] = w.N
+    bad[1, 1, 50] = w.N + 1000
+    clean = np.where(bad >= w.N, -1, bad).astype(np.int32)
+    got = run_gpu(w, 0, bad)
+    exp = ref(w.q, w.kv_host(), w.sink, clean, w.scale)
+    assert_close(got, exp, "beyond-N skipped")
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_split_counts_agree(ref, S):
+    w = wl.make_decode(B=4)
+    check(ref, w, S, what=f"decode B=4 S={S}")
+
+
+def test_bitwise_deterministic():
+    w = wl.make_decode(B=8)
+    for S in (1, 4):
+        runs = [run_gpu(w, S) for _ in range(3)]
+        assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
+
+
+def test_check_idxs_counts_out_of_range():
+    torch = torch_mod()
+    from sparse_top_latent_amd import check_idxs
+    w = wl.make_random(14, 3, 4, 8, 128, 100, 50, p_unused=0.2)
+    bad = w.idxs.copy()
+    bad[0, 0, 0] = 100
+    bad[2, 3, 49] = 12345
+    bad[1, 2, 7] = 100
+    assert check_idxs(torch.from_numpy(w.idxs).cuda(), w.N) == 0
+    assert check_idxs(torch.from_numpy(bad).cuda(), w.N) == 3
+
+
+# --------------------------------------------------------- full-size workloads
+# Same launch configuration as bench.py: num_splits=0 (planned by the library).
+
+def sampled_check(ref, w, queries, got):
+    """Oracle on the listed queries one by one; same bar as assert_close."""
+    exps = []
+    for (b, t) in queries:
+        q1, kv1, i1 = w.query_slice(b, t)
+        exps.append(ref(q1, kv1, w.sink, i1, w.scale)[0, 0])
+    exp = np.stack(exps)
+    sub = np.stack([got[b, t] for (b, t) in queries])
+    assert_close(sub, exp, f"{w.name} sampled {len(queries)}")
+
+
+@pytest.mark.parametrize("name", ["decode", "long", "window"])
+def test_full_config_every_query(ref, name):
+    w = wl.make(name)
+    got = run_gpu(w, 0)
+    exp = ref(w.q, w.kv_host(), w.sink, w.idxs, w.scale) if name == "window" else None
+    if exp is not None:
+        assert_close(got, exp, name)
+    else:
+        sampled_check(ref, w, [(b, 0) for b in range(w.B)], got)
+
+
+def test_full_prefill_sampled(ref):
+    w = wl.make("prefill")
+    got = run_gpu(w, 0)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(0)
+    ts = sorted(set([0, 1, 2, 126, 127, 128, 129, 1023, 2048, 4094, 4095]
+                    + list(rng.choice(4096, 37, replace=False))))
+    sampled_check(ref, w, [(0, int(t)) for t in ts], got)
+
+
+def test_full_ragged_sampled(ref):
+    w = wl.make("ragged")
+    got = run_gpu(w, 0)
+    assert np.isfinite(got).all()
+    valid = (w.idxs >= 0).sum(-1)[:, 0]
+    order = np.argsort(valid)
+    pick = sorted(set(list(order[:16]) + list(order[-16:]) +
+                      list(np.random.default_rng(1).choice(256, 32, replace=False))))
+    sampled_check(ref, w, [(int(b), 0) for b in pick], got)
