@@ -83,50 +83,103 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// Compacts the valid entries (0 <= idx < N) of one list into `list`, keeping
-// their order, and returns how many there are.  All threads take part.
+// a1: index decode + compaction.  The list is read in groups of EG rounds of
+// NT entries: every thread loads its (up to) EG entries of a group at once
+// (one memory round trip), a ballot per round gives each valid entry its
+// slot, and one barrier publishes the per-wave counts.  Entries keep their
+// order.  Returns the number of valid entries (0 <= idx < N).
 template <int NT>
 __device__ int compact_list(const int32_t *__restrict__ lst, int K, int64_t N, int32_t *list,
-                            int32_t *wave_cnt) {
+                            int32_t *cnt /* [EG][NT/64] */) {
     constexpr int NWV = NT / 64;
+    constexpr int EG = 8;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     int base = 0;
-    for (int k0 = 0; k0 < K; k0 += NT) {
-        const int k = k0 + tid;
-        const int v = k < K ? lst[k] : -1;
-        const bool ok = v >= 0 && (int64_t)v < N;
-        const uint64_t mask = __ballot(ok);
-        const int before = __popcll(mask & ((1ull << lane) - 1ull));
-        if (lane == 0) wave_cnt[wid] = __popcll(mask);
-        __syncthreads();
-        int off = base, total = 0;
+    for (int k0 = 0; k0 < K; k0 += EG * NT) {
+        int v[EG];
+        uint64_t mask[EG];
 #pragma unroll
-        for (int w = 0; w < NWV; ++w) {
-            const int c = wave_cnt[w];
-            off += w < wid ? c : 0;
-            total += c;
+        for (int r = 0; r < EG; ++r) {
+            const int k = k0 + r * NT + tid;
+            v[r] = k < K ? lst[k] : -1;
         }
-        if (ok) list[off + before] = v;
-        base += total;
+#pragma unroll
+        for (int r = 0; r < EG; ++r) {
+            mask[r] = __ballot(v[r] >= 0 && (int64_t)v[r] < N);
+            if (lane == 0) cnt[r * NWV + wid] = __popcll(mask[r]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < EG; ++r) {
+            int before_waves = 0, round = 0;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) {
+                const int c = cnt[r * NWV + w];
+                before_waves += w < wid ? c : 0;
+                round += c;
+            }
+            if ((mask[r] >> lane) & 1ull)
+                list[base + before_waves + __popcll(mask[r] & ((1ull << lane) - 1ull))] = v[r];
+            base += round;
+        }
         __syncthreads();
     }
     return base;
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
+// One LDS-DMA wave instruction: every lane fetches 16 bytes from its own
+// global address; they land at lds_base + 16 * lane.  Issued through asm so
+// the compiler does not order later LDS reads behind it (it would otherwise
+// wait for every DMA in flight before any LDS read); the ring below waits for
+// exactly the chunk it needs with wait_vm_ahead.
+__device__ __forceinline__ void lds_dma16(const void *gptr, const LDS_AS void *lds_base) {
+    // the LDS base is wave-uniform; readfirstlane puts it in an SGPR for M0
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(m0)
+                 : "memory", "m0");
+}
+
+// s_waitcnt with a vmcnt chosen at run time among the few values the ring can
+// need (the immediate must be a constant).  Waits until at most `n` vector
+// memory operations of this wave are still outstanding.
+template <int STEP, int MAXA>
+__device__ __forceinline__ void wait_vm_ahead(int ahead) {
+    static_assert(STEP > 0 && MAXA >= 0 && MAXA <= 2 && MAXA * STEP <= 63, "vmcnt is 6 bits");
+    if (MAXA >= 2 && ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * STEP) : "memory");
+    else if (MAXA >= 1 && ahead >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(STEP) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Work split: a workgroup holds NHQ groups of 16 heads; each group is served
+// by a pair of waves, one per half of the head dimension.  For QK^T a wave
+// sums over its half of d and the pair adds the two partial scores through
+// LDS, so both waves of the pair hold the same scores and run the same
+// softmax; for PV each wave produces its half of the output columns.  A wave
+// therefore keeps only 16 x D/2 accumulators and 16 x D/2 query values in
+// registers, which leaves room for two waves per SIMD.
+template <int D, int NHQ>
+__global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
+    constexpr int NW = 2 * NHQ;            // waves per workgroup
     constexpr int NT = NW * 64;
     constexpr int ROWB = D * 2;            // bytes per row
     constexpr int CPR = D / 8;             // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;          // rows per LDS-DMA wave instruction
     constexpr int NINS = KC / RPI;         // DMA wave instructions per chunk
-    constexpr int DS = D / 32;             // MFMA k-steps over d
-    constexpr int DT = D / 16;             // 16-wide d tiles of the output
+    constexpr int IPW = NINS / NW;         // ... per wave
+    constexpr int DSH = D / 64;            // MFMA k-steps over one half of d
+    constexpr int DTH = D / 32;            // 16-wide output tiles in one half of d
+    // LDS ring depth (chunks): up to 4, as long as the DMA instructions of the
+    // chunks in flight fit the 6-bit vmcnt
+    constexpr int NBUF = 2 + (63 / IPW >= 2 ? 2 : 63 / IPW);
     static_assert(CPR >= 16 && 64 % CPR == 0, "row swizzle needs D in {128, 256, 512}");
+    static_assert(NINS % NW == 0, "DMA instructions must split evenly over the waves");
 
-    __shared__ __attribute__((aligned(16))) uint8_t tile[2][KC * ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][KC * ROWB];
+    __shared__ __attribute__((aligned(16))) float xbuf[NW][64 * 8];  // partial scores
     __shared__ int32_t list[LIST_CAP];
-    __shared__ int32_t wave_cnt[NW];
+    __shared__ int32_t cnt[8 * NW];
 
     // XCD-aware unit order: consecutive units (the splits and head groups of
     // one query, or neighbouring queries) run on the same XCD and share its L2.
@@ -139,87 +192,110 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
     const int b = qi / p.T;
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int hq = wid >> 1;      // head group of this wave
+    const int dh = wid & 1;       // half of d this wave covers
     const int g = lane >> 4;      // 16-lane block of the wave
     const int li = lane & 15;
 
+    // a3: this lane's head and its half of the query row, held as MFMA B
+    // operands: qf[k] = q[h, 32kk + 8g .. 32kk + 8g + 7] with kk = dh*DSH + k.
+    // Issued before the list loads: the wait for the list then covers q too,
+    // so the chunk loop never waits on q behind the row DMAs.
+    const int h = hg * (NHQ * 16) + hq * 16 + li;
+    const bool h_ok = h < p.H;
+    bf16x8_t qf[DSH];
+    {
+        const uint16_t *qrow = p.q + ((int64_t)qi * p.H + (h_ok ? h : 0)) * D + dh * (D / 2);
+#pragma unroll
+        for (int k = 0; k < DSH; ++k)
+            qf[k] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(qrow + 32 * k + 8 * g));
+    }
+
     // a1: decode and compact the list, then take this split's slice.
-    const int n = compact_list<NT>(p.idxs + (int64_t)qi * p.K, p.K, p.N, list, wave_cnt);
+    const int n = compact_list<NT>(p.idxs + (int64_t)qi * p.K, p.K, p.N, list, cnt);
+    // q has landed before the row ring starts (the list wait usually covers it
+    // already).  This wait is the compiler-visible form, so the compiler does
+    // not place waits for q inside the chunk loop, where they would also wait
+    // for the row DMAs in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
     const int lo = (int)(((int64_t)n * s) / p.S);
     const int hi = (int)(((int64_t)n * (s + 1)) / p.S);
     const int nchunks = (hi - lo + KC - 1) / KC;
 
-    // a3: this lane's head and its query row, held as MFMA B operands:
-    // qf[k] = q[h, 32k + 8g .. 32k + 8g + 7].
-    const int h = hg * (NW * 16) + wid * 16 + li;
-    const bool h_ok = h < p.H;
-    bf16x8_t qf[DS];
-    {
-        const uint16_t *qrow = p.q + ((int64_t)qi * p.H + (h_ok ? h : 0)) * D;
-#pragma unroll
-        for (int k = 0; k < DS; ++k) {
-            u32x4_t v = *(const u32x4_t *)(qrow + 32 * k + 8 * g);
-            if (!h_ok) v = u32x4_t{0, 0, 0, 0};
-            qf[k] = __builtin_bit_cast(bf16x8_t, v);
-        }
-    }
-
-    // Softmax state of head h (log2 units).  The non-split path starts from
-    // the sink: max = sink, denominator = 1 (counted once, in block 0).
-    float m = -INFINITY, lsum = 0.f;
-    if (p.S == 1 && p.sink != nullptr && h_ok) {
-        m = p.sink[h] * LOG2E;
-        lsum = g == 0 ? 1.f : 0.f;
-    }
-    f32x4_t o[DT];
-#pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
     const uint16_t *kvb = p.kv + (int64_t)b * p.N * D;
 
-    // a2: gather the rows of chunk c into LDS buffer `buf` with LDS-DMA.
+    // a2: gather the rows of chunk c into ring slot c % NBUF with LDS-DMA.
     // Each wave instruction moves RPI whole rows: lane l lands at byte 16*l of
     // the instruction's 1 KB, i.e. row r = l / CPR at position l % CPR, so it
     // fetches the row's chunk (position ^ swz(r)).  Tail slots repeat the
     // chunk's first row; their scores are masked to -inf below.
-    auto stage = [&](int c, int buf) {
+    auto stage = [&](int c) {
         const int e0 = lo + c * KC;
-        static_assert(NINS % NW == 0, "DMA instructions must split evenly over the waves");
+        uint8_t *buf = &tile[c % NBUF][0];
 #pragma unroll
-        for (int k = 0; k < NINS / NW; ++k) {
+        for (int k = 0; k < IPW; ++k) {
             const int ii = k * NW + wid;
             const int r = ii * RPI + lane / CPR;
             const int pos = lane % CPR;
             const int e = e0 + r;
             const int row = list[e < hi ? e : e0];
             const uint16_t *src = kvb + (int64_t)row * D + ((pos ^ swz(r)) << 3);
-            LDS_AS void *dst = (LDS_AS void *)((LDS_AS uint8_t *)&tile[buf][0] + ii * 1024);
-            __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+            LDS_AS void *dst = (LDS_AS void *)((LDS_AS uint8_t *)buf + ii * 1024);
+            lds_dma16(src, dst);
         }
     };
+#pragma unroll
+    for (int c = 0; c < NBUF - 1; ++c)
+        if (c < nchunks) stage(c);
 
-    if (nchunks > 0) stage(0, 0);
+    if (!h_ok) {
+#pragma unroll
+        for (int k = 0; k < DSH; ++k) qf[k] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+    }
+
+    // Softmax state of head h (log2 units), identical in both waves of the
+    // pair.  The non-split path starts from the sink: max = sink, denominator
+    // = 1 (counted once per wave, in block 0).
+    float m = -INFINITY, lsum = 0.f;
+    if (p.S == 1 && p.sink != nullptr && h_ok) {
+        m = p.sink[h] * LOG2E;
+        lsum = g == 0 ? 1.f : 0.f;
+    }
+    f32x4_t o[DTH];
+#pragma unroll
+    for (int t = 0; t < DTH; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    LDS_AS float *xmine = (LDS_AS float *)&xbuf[wid][lane * 8];
+    const LDS_AS float *xpeer = (const LDS_AS float *)&xbuf[wid ^ 1][lane * 8];
 
     for (int c = 0; c < nchunks; ++c) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // chunk c has landed once at most `ahead` later chunks are pending
+        wait_vm_ahead<IPW, NBUF - 2>(min(NBUF - 2, nchunks - 1 - c));
         __syncthreads();
-        if (c + 1 < nchunks) stage(c + 1, (c + 1) & 1);
+        if (c + NBUF - 1 < nchunks) stage(c + NBUF - 1);
 
-        const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c & 1][0];
-        const int cnt = min(KC, hi - (lo + c * KC));
+        const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NBUF][0];
+        const int cnt_c = min(KC, hi - (lo + c * KC));
 
-        // a4: S^T[j, h] for j in the chunk (two 16-row tiles).
+        // a4: partial S^T[j, h] over this wave's half of d (two 16-row tiles).
         f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int k = 0; k < DS; ++k) {
+        for (int k = 0; k < DSH; ++k) {
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
                 const int r = jt * 16 + li;
-                const int pos = (4 * k + g) ^ swz(r);
+                const int pos = (4 * (dh * DSH + k) + g) ^ swz(r);
                 const u32x4_t a = *(const LDS_AS u32x4_t *)(T + r * ROWB + pos * 16);
                 sacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8_t, a), qf[k], sacc[jt], 0, 0, 0);
             }
         }
+        // the pair adds its two halves (a + b == b + a, so both waves agree)
+        *(LDS_AS f32x4_t *)(xmine) = sacc[0];
+        *(LDS_AS f32x4_t *)(xmine + 4) = sacc[1];
+        __syncthreads();
+        sacc[0] += *(const LDS_AS f32x4_t *)(xpeer);
+        sacc[1] += *(const LDS_AS f32x4_t *)(xpeer + 4);
 
         // a5: mask + online sink-softmax.  Lane (li, g) holds rows
         // j = 16 jt + 4 g + i of head h.
@@ -230,7 +306,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = 16 * jt + 4 * g + i;
-                const float x = j < cnt ? sacc[jt][i] * p.qk_scale_log2 : -INFINITY;
+                const float x = j < cnt_c ? sacc[jt][i] * p.qk_scale_log2 : -INFINITY;
                 sv[jt * 4 + i] = x;
                 cmax = fmaxf(cmax, x);
             }
@@ -242,7 +318,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
             const float alpha = exp2_fast(m - mnew);
             lsum *= alpha;
 #pragma unroll
-            for (int t = 0; t < DT; ++t) o[t] *= alpha;
+            for (int t = 0; t < DTH; ++t) o[t] *= alpha;
             m = mnew;
         }
         // The weights enter the value product as bf16; the denominator sums
@@ -259,10 +335,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
         lsum += psum;
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
 
-        // a6: O^T[d, h] += V^T[d, j] P^T[j, h].  A operand through transpose
-        // loads: lane i of block g addresses row 4g + i/4 (and +16), columns
-        // 16t + 4(i%4) .. +3; the load hands lane i column 16t + i of rows
-        // 4g..4g+3, matching the weight slots j = 4g + e and 16 + 4g + e.
+        // a6: O^T[d, h] += V^T[d, j] P^T[j, h] for this wave's half of d.
+        // A operand through transpose loads: lane i of block g addresses row
+        // 4g + i/4 (and +16), columns 16t + 4(i%4) .. +3; the load hands lane i
+        // column 16t + i of rows 4g..4g+3, matching the weight slots
+        // j = 4g + e and 16 + 4g + e.
         {
             const int r0 = 4 * g + (li >> 2);
             const int sw = swz(r0);  // rows r0 and r0 + 16 share the swizzle
@@ -270,8 +347,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
             const LDS_AS uint8_t *R0 = T + r0 * ROWB + half;
             const LDS_AS uint8_t *R1 = R0 + 16 * ROWB;
 #pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                const int pos = ((2 * t + ((li >> 1) & 1)) ^ sw) * 16;
+            for (int t = 0; t < DTH; ++t) {
+                const int tt = dh * DTH + t;
+                const int pos = ((2 * tt + ((li >> 1) & 1)) ^ sw) * 16;
                 const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R0 + pos));
                 const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R1 + pos));
                 const bf16x8_t a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -280,25 +358,25 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
         }
     }
 
-    // a7 / a8: epilogue.  Lane (li, g) holds O^T[16t + 4g + i, h].
+    // a7 / a8: epilogue.  Lane (li, g) holds O^T[dh*D/2 + 16t + 4g + i, h].
     float ltot = lsum + shfl_xor_f(lsum, 16);
     ltot += shfl_xor_f(ltot, 32);
     if (!h_ok) return;
     if (p.S == 1) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        uint16_t *orow = p.out + ((int64_t)qi * p.H + h) * D + 4 * g;
+        uint16_t *orow = p.out + ((int64_t)qi * p.H + h) * D + dh * (D / 2) + 4 * g;
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
+        for (int t = 0; t < DTH; ++t) {
             const u32x2_t w = {pack2_bf16(o[t][0] * inv, o[t][1] * inv),
                                pack2_bf16(o[t][2] * inv, o[t][3] * inv)};
             *(u32x2_t *)(orow + 16 * t) = w;
         }
     } else {
         const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
-        float *orow = p.ws_o + slot * D + 4 * g;
+        float *orow = p.ws_o + slot * D + dh * (D / 2) + 4 * g;
 #pragma unroll
-        for (int t = 0; t < DT; ++t) *(f32x4_t *)(orow + 16 * t) = o[t];
-        if (g == 0) {
+        for (int t = 0; t < DTH; ++t) *(f32x4_t *)(orow + 16 * t) = o[t];
+        if (g == 0 && dh == 0) {
             p.ws_m[slot] = m;
             p.ws_l[slot] = ltot;
         }
@@ -370,7 +448,8 @@ int device_cu_count() {
     return cache[dev];
 }
 
-int waves_for(int H) { return H >= 64 ? 4 : H > 16 ? (H > 32 ? 4 : 2) : 1; }
+// groups of 16 heads per workgroup
+int quads_for(int H) { return H > 32 ? 4 : H > 16 ? 2 : 1; }
 
 int check_dims(const sa_dims *d) {
     if (d == nullptr) return SA_ERR_NULL;
@@ -403,7 +482,7 @@ WsLayout ws_layout(const sa_dims *d, int S) {
 int plan_splits(const sa_dims *d) {
     const int cus = device_cu_count();
     if (cus < 0) return -SA_ERR_HIP;
-    const int nw = waves_for(d->H);
+    const int nw = quads_for(d->H);
     const int64_t hg = (d->H + 16 * nw - 1) / (16 * nw);
     const int64_t units = queries(d) * hg;
     if (units <= 0 || units >= cus) return 1;
@@ -414,10 +493,10 @@ int plan_splits(const sa_dims *d) {
     return (int)(S < 1 ? 1 : S);
 }
 
-template <int D, int NW>
+template <int D, int NHQ>
 hipError_t launch_fwd(const FwdParams &p, hipStream_t stream) {
     const int grid = 8 * p.per_xcd;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW>), dim3(grid), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ>), dim3(grid), dim3(NHQ * 128), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -497,7 +576,7 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
     p.H = d->H;
     p.K = d->K;
     p.S = S;
-    const int nw = waves_for(d->H);
+    const int nw = quads_for(d->H);
     p.HG = (d->H + 16 * nw - 1) / (16 * nw);
     const int64_t units = queries(d) * p.HG * S;
     p.units = (int32_t)units;
@@ -507,7 +586,7 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
 }
 
 hipError_t run_fwd(const FwdParams &p, int D, int H, hipStream_t stream) {
-    const int nw = waves_for(H);
+    const int nw = quads_for(H);
     switch (D) {
         case 128: return launch_fwd_d<128>(nw, p, stream);
         case 256: return launch_fwd_d<256>(nw, p, stream);
@@ -516,7 +595,7 @@ hipError_t run_fwd(const FwdParams &p, int D, int H, hipStream_t stream) {
 }
 
 bool units_fit(const sa_dims *d, int S) {
-    const int nw = waves_for(d->H);
+    const int nw = quads_for(d->H);
     const int64_t hg = (d->H + 16 * nw - 1) / (16 * nw);
     return queries(d) * hg * S <= (int64_t)0x7FFFFFF0;
 }
