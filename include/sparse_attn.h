@@ -75,8 +75,10 @@ enum sa_status {
 int32_t sparse_attn_plan_splits(const sa_dims *d);
 
 /* Bytes of workspace sparse_attn_fwd needs for `num_splits` (0 = the planned
- * count): 0 for one split, else float32 partial outputs [B*T, S, H, D] plus
- * the running max and denominator [B*T, S, H] each.  Returns 0 on bad dims. */
+ * count): 0 for one split, else each split's output normalised by its own
+ * denominator, float32 [B*T, S, H, D], plus its running max (log2 units) and
+ * denominator, float32 [B*T, S, H] each, every part padded to 256 bytes.
+ * Returns 0 on bad dims. */
 size_t sparse_attn_workspace_bytes(const sa_dims *d, int32_t num_splits);
 
 /* The whole step: out = sparse_attn(q, kv, sink, idxs, scale).

@@ -8,16 +8,17 @@
 //   attn_fwd    one workgroup per (query, head group, split).  Steps:
 //               index decode + compaction of the query's list into LDS, a
 //               per-split slice of the valid entries, then chunks of 32 rows:
-//               LDS-DMA gather of the rows (16 B per lane, double buffered),
+//               LDS-DMA gather of the rows (16 B per lane, a 4-chunk ring),
 //               S^T = K Q^T on 16x16x32 bf16 MFMAs, the online sink-softmax in
 //               float32, O^T += V^T P^T on MFMAs with V read through LDS
-//               transpose loads.  Epilogue: bf16 output, or float32 partials.
+//               transpose loads.  Epilogue: bf16 output, or float32 partials
+//               of a split, staged through LDS into whole-row stores.
 //   combine     log-sum-exp merge of split partials plus the sink -> bf16.
 //   check_idxs  counts entries >= N.
 //
-// Work split inside a workgroup: wave w owns 16 heads for both products, so
-// the softmax of a head never leaves its wave; the four waves share one LDS
-// copy of each row chunk (one HBM read per row per workgroup).
+// Work split inside a workgroup: a pair of waves owns 16 heads (one wave per
+// half of the head dimension); all waves share one LDS copy of each row chunk
+// (one HBM read per row per workgroup).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -53,7 +54,7 @@ struct FwdParams {
     const float *sink;
     const int32_t *idxs;
     uint16_t *out;     // non-split path
-    float *ws_o;       // split path: [Q, S, H, D]
+    float *ws_o;       // split path: [Q, S, H, D], each split normalised by its ws_l
     float *ws_m;       // [Q, S, H] running max, log2 units
     float *ws_l;       // [Q, S, H] denominator relative to ws_m
     int64_t N;
@@ -63,11 +64,19 @@ struct FwdParams {
 };
 
 // Row swizzle of the 16-byte chunks inside a row of the LDS tile: chunk c of
-// row r lives at position c ^ swz(r).  Rows are 2*D bytes apart (a multiple
-// of 256 B, so every row starts on the same bank); the XOR spreads the 16
-// rows read by a b128 MFMA-operand load, and the 4x2 chunks read by each
-// 16-lane block of a transpose load, over distinct banks.
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// row r lives at position c ^ swz<CPR>(r).  gfx950's LDS serves a b128 read
+// 32 lanes (512 bytes) per pass, so the 32 lanes of a half-wave must land in
+// 32 distinct 16-byte bank slots (slot = byte address / 16 mod 32).  The
+// operand load of QK^T has lanes (row li, chunk c0 or c0^1): an even swizzle
+// keeps the two chunk parities apart and spreads the 16 rows.  Rows of 1 KB
+// or 512 B all start on slot 0, so swz = 2r mod 32; 256-byte rows alternate
+// between slot 0 and 16, so the rows of one parity share 2*(r/2) mod 16.  The
+// transpose loads of PV (rows 4g + i/4, chunk pairs 2t, 2t+1) are spread by
+// the same swizzle.  Rows r and r + 16 share a swizzle.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    return CPR >= 32 ? (2 * r) & 31 : (2 * (r >> 1)) & 15;
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -177,7 +186,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     static_assert(NINS % NW == 0, "DMA instructions must split evenly over the waves");
 
     __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][KC * ROWB];
-    __shared__ __attribute__((aligned(16))) float xbuf[NW][64 * 8];  // partial scores
+    __shared__ __attribute__((aligned(16))) f32x4_t xbuf[NW][2][64];  // partial scores
     __shared__ int32_t list[LIST_CAP];
     __shared__ int32_t cnt[8 * NW];
 
@@ -239,7 +248,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             const int pos = lane % CPR;
             const int e = e0 + r;
             const int row = list[e < hi ? e : e0];
-            const uint16_t *src = kvb + (int64_t)row * D + ((pos ^ swz(r)) << 3);
+            const uint16_t *src = kvb + (int64_t)row * D + ((pos ^ swz<CPR>(r)) << 3);
             LDS_AS void *dst = (LDS_AS void *)((LDS_AS uint8_t *)buf + ii * 1024);
             lds_dma16(src, dst);
         }
@@ -265,8 +274,8 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int t = 0; t < DTH; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    LDS_AS float *xmine = (LDS_AS float *)&xbuf[wid][lane * 8];
-    const LDS_AS float *xpeer = (const LDS_AS float *)&xbuf[wid ^ 1][lane * 8];
+    LDS_AS f32x4_t *xmine = (LDS_AS f32x4_t *)&xbuf[wid][0][lane];
+    const LDS_AS f32x4_t *xpeer = (const LDS_AS f32x4_t *)&xbuf[wid ^ 1][0][lane];
 
     for (int c = 0; c < nchunks; ++c) {
         // chunk c has landed once at most `ahead` later chunks are pending
@@ -284,18 +293,18 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
                 const int r = jt * 16 + li;
-                const int pos = (4 * (dh * DSH + k) + g) ^ swz(r);
+                const int pos = (4 * (dh * DSH + k) + g) ^ swz<CPR>(r);
                 const u32x4_t a = *(const LDS_AS u32x4_t *)(T + r * ROWB + pos * 16);
                 sacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8_t, a), qf[k], sacc[jt], 0, 0, 0);
             }
         }
         // the pair adds its two halves (a + b == b + a, so both waves agree)
-        *(LDS_AS f32x4_t *)(xmine) = sacc[0];
-        *(LDS_AS f32x4_t *)(xmine + 4) = sacc[1];
+        xmine[0] = sacc[0];
+        xmine[64] = sacc[1];
         __syncthreads();
-        sacc[0] += *(const LDS_AS f32x4_t *)(xpeer);
-        sacc[1] += *(const LDS_AS f32x4_t *)(xpeer + 4);
+        sacc[0] += xpeer[0];
+        sacc[1] += xpeer[64];
 
         // a5: mask + online sink-softmax.  Lane (li, g) holds rows
         // j = 16 jt + 4 g + i of head h.
@@ -342,7 +351,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         // j = 4g + e and 16 + 4g + e.
         {
             const int r0 = 4 * g + (li >> 2);
-            const int sw = swz(r0);  // rows r0 and r0 + 16 share the swizzle
+            const int sw = swz<CPR>(r0);  // rows r0 and r0 + 16 share the swizzle
             const int half = (li & 1) * 8;
             const LDS_AS uint8_t *R0 = T + r0 * ROWB + half;
             const LDS_AS uint8_t *R1 = R0 + 16 * ROWB;
@@ -359,32 +368,70 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     }
 
     // a7 / a8: epilogue.  Lane (li, g) holds O^T[dh*D/2 + 16t + 4g + i, h].
+    // Every output (final, or a split's partial) is normalised by its own
+    // denominator, then staged through the (now idle) LDS ring so that each
+    // wave instruction stores 1 KB of contiguous row: the final output as
+    // bf16, a split's partial as float32.  In LDS, 16-byte chunk c of head row
+    // hl sits at position c ^ swz(hl), which keeps the 16 rows written by one
+    // store instruction on distinct banks.
     float ltot = lsum + shfl_xor_f(lsum, 16);
     ltot += shfl_xor_f(ltot, 32);
-    if (!h_ok) return;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    __syncthreads();  // every wave is done with the ring; reuse it for staging
+    LDS_AS uint8_t *stage_out = (LDS_AS uint8_t *)&tile[0][0];
+    const int hl = hq * 16 + li;  // head row within the workgroup
+    const int hbase = hg * (NHQ * 16);
     if (p.S == 1) {
-        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        uint16_t *orow = p.out + ((int64_t)qi * p.H + h) * D + dh * (D / 2) + 4 * g;
+        constexpr int C16 = D / 8;  // 16-byte chunks per bf16 row
+        static_assert(NHQ * 16 * D * 2 <= NBUF * KC * ROWB, "bf16 staging fits in the ring");
+        LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
 #pragma unroll
         for (int t = 0; t < DTH; ++t) {
+            const int col = dh * (D / 2) + 16 * t + 4 * g;  // first of 4 columns
+            const int pos = (col >> 3) ^ swz<C16>(hl);
             const u32x2_t w = {pack2_bf16(o[t][0] * inv, o[t][1] * inv),
                                pack2_bf16(o[t][2] * inv, o[t][3] * inv)};
-            *(u32x2_t *)(orow + 16 * t) = w;
+            *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
+        }
+        __syncthreads();
+        uint16_t *dst = p.out + (int64_t)qi * p.H * D;
+        for (int i = tid; i < NHQ * 16 * C16; i += NT) {
+            const int r = i / C16, pos = i % C16;
+            const u32x4_t v = *(const LDS_AS u32x4_t *)(stage_out + r * (D * 2) + pos * 16);
+            if (hbase + r < p.H)
+                *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v;
         }
     } else {
-        const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
-        float *orow = p.ws_o + slot * D + dh * (D / 2) + 4 * g;
+        constexpr int C32 = D / 4;  // 16-byte chunks per float32 row
+        static_assert(NHQ * 16 * D * 4 <= NBUF * KC * ROWB, "float32 staging fits in the ring");
+        LDS_AS uint8_t *Rrow = stage_out + hl * (D * 4);
 #pragma unroll
-        for (int t = 0; t < DTH; ++t) *(f32x4_t *)(orow + 16 * t) = o[t];
-        if (g == 0 && dh == 0) {
+        for (int t = 0; t < DTH; ++t) {
+            const int col = dh * (D / 2) + 16 * t + 4 * g;
+            const int pos = (col >> 2) ^ swz<C32>(hl);
+            *(LDS_AS f32x4_t *)(Rrow + pos * 16) = o[t] * inv;
+        }
+        if (g == 0 && dh == 0 && h_ok) {
+            const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
             p.ws_m[slot] = m;
             p.ws_l[slot] = ltot;
+        }
+        __syncthreads();
+        float *dst = p.ws_o + ((int64_t)qi * p.S + s) * p.H * D;
+        for (int i = tid; i < NHQ * 16 * C32; i += NT) {
+            const int r = i / C32, pos = i % C32;
+            const f32x4_t v = *(const LDS_AS f32x4_t *)(stage_out + r * (D * 4) + pos * 16);
+            if (hbase + r < p.H)
+                *(f32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C32>(r)) << 2)) = v;
         }
     }
 }
 
-// a9: out[q, h, :] = (sum_s 2^(m_s - M) O_s + 0) / (2^(sink - M) + sum_s 2^(m_s - M) l_s),
-// M = max(sink, max_s m_s), all in log2 units.  One thread per 4 outputs.
+// a9: log-sum-exp merge of the splits.  Split s holds p_s (its output
+// normalised by its own denominator l_s, float32), its max m_s and l_s (log2
+// units).  With M = max(sink, max_s m_s) and
+// L = 2^(sink - M) + sum_s 2^(m_s - M) l_s, out = sum_s (2^(m_s - M) l_s / L) p_s.
+// One wave per (query, head) row when D = 512; each lane merges 8 columns.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ws_o,
                                                       const float *__restrict__ ws_m,
@@ -392,30 +439,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                                                       const float *__restrict__ sink,
                                                       uint16_t *__restrict__ out, int64_t QH,
                                                       int H, int S) {
-    constexpr int DQ = D / 4;
+    constexpr int LPR = D / 8;  // lanes per row
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= QH * DQ) return;
-    const int64_t qh = idx / DQ;
-    const int dq = (int)(idx % DQ);
+    if (idx >= QH * LPR) return;
+    const int64_t qh = idx / LPR;
+    const int c8 = (int)(idx % LPR) * 8;
     const int64_t qi = qh / H;
     const int h = (int)(qh % H);
     const float mz = sink != nullptr ? sink[h] * LOG2E : -INFINITY;
     float mx = mz;
     for (int s = 0; s < S; ++s) mx = fmaxf(mx, ws_m[(qi * S + s) * H + h]);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
     if (mx != -INFINITY) {
-        L = sink != nullptr ? exp2_fast(mz - mx) : 0.f;
+        float L = sink != nullptr ? exp2_fast(mz - mx) : 0.f;
+        for (int s = 0; s < S; ++s)
+            L += exp2_fast(ws_m[(qi * S + s) * H + h] - mx) * ws_l[(qi * S + s) * H + h];
+        const float invL = L > 0.f ? 1.f / L : 0.f;
         for (int s = 0; s < S; ++s) {
             const int64_t slot = (qi * S + s) * H + h;
-            const float w = exp2_fast(ws_m[slot] - mx);
-            L += w * ws_l[slot];
-            acc += w * *(const f32x4_t *)(ws_o + slot * D + 4 * dq);
+            const float c = exp2_fast(ws_m[slot] - mx) * ws_l[slot] * invL;
+            a0 += c * *(const f32x4_t *)(ws_o + slot * D + c8);
+            a1 += c * *(const f32x4_t *)(ws_o + slot * D + c8 + 4);
         }
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const u32x2_t w = {pack2_bf16(acc[0] * inv, acc[1] * inv), pack2_bf16(acc[2] * inv, acc[3] * inv)};
-    *(u32x2_t *)(out + qh * D + 4 * dq) = w;
+    const u32x4_t w = {pack2_bf16(a0[0], a0[1]), pack2_bf16(a0[2], a0[3]),
+                       pack2_bf16(a1[0], a1[1]), pack2_bf16(a1[2], a1[3])};
+    *(u32x4_t *)(out + qh * D + c8) = w;
 }
 
 __global__ __launch_bounds__(256) void check_idxs_kernel(const int32_t *__restrict__ idxs,
@@ -512,7 +561,7 @@ hipError_t launch_fwd_d(int nw, const FwdParams &p, hipStream_t stream) {
 hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
                           const void *ws, const WsLayout &L, hipStream_t stream) {
     const int64_t QH = queries(d) * d->H;
-    const int64_t threads = QH * (d->D / 4);
+    const int64_t threads = QH * (d->D / 8);
     const unsigned grid = (unsigned)((threads + 255) / 256);
     const float *wo = (const float *)((const uint8_t *)ws + L.o_off);
     const float *wm = (const float *)((const uint8_t *)ws + L.m_off);
