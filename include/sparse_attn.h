@@ -76,9 +76,10 @@ int32_t sparse_attn_plan_splits(const sa_dims *d);
 
 /* Bytes of workspace sparse_attn_fwd needs for `num_splits` (0 = the planned
  * count): 0 for one split, else each split's output normalised by its own
- * denominator, float32 [B*T, S, H, D], plus its running max (log2 units) and
- * denominator, float32 [B*T, S, H] each, every part padded to 256 bytes.
- * Returns 0 on bad dims. */
+ * denominator as fp16 [B*T, S, H, D] (each half row divided by a power of two
+ * so that no value overflows), its running max (log2 units) and denominator,
+ * float32 [B*T, S, H] each, and the half-row scales, float32 [B*T, S, H, 2];
+ * every part padded to 256 bytes.  Returns 0 on bad dims. */
 size_t sparse_attn_workspace_bytes(const sa_dims *d, int32_t num_splits);
 
 /* The whole step: out = sparse_attn(q, kv, sink, idxs, scale).

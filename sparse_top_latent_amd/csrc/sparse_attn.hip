@@ -11,8 +11,9 @@
 //               LDS-DMA gather of the rows (16 B per lane, a 4-chunk ring),
 //               S^T = K Q^T on 16x16x32 bf16 MFMAs, the online sink-softmax in
 //               float32, O^T += V^T P^T on MFMAs with V read through LDS
-//               transpose loads.  Epilogue: bf16 output, or float32 partials
-//               of a split, staged through LDS into whole-row stores.
+//               transpose loads.  Epilogue: bf16 output, or a split's fp16
+//               partial (power-of-two scaled per half row), staged through
+//               LDS into whole-row stores.
 //   combine     log-sum-exp merge of split partials plus the sink -> bf16.
 //   check_idxs  counts entries >= N.
 //
@@ -54,9 +55,11 @@ struct FwdParams {
     const float *sink;
     const int32_t *idxs;
     uint16_t *out;     // non-split path
-    float *ws_o;       // split path: [Q, S, H, D], each split normalised by its ws_l
+    uint16_t *ws_o;    // split path: [Q, S, H, D] fp16, each split normalised by its ws_l
+                       // and divided by the power of two ws_x of its half row
     float *ws_m;       // [Q, S, H] running max, log2 units
     float *ws_l;       // [Q, S, H] denominator relative to ws_m
+    float *ws_x;       // [Q, S, H, 2] power-of-two scale of each half row of ws_o
     int64_t N;
     int32_t T, H, K;
     int32_t S, HG, units, per_xcd;
@@ -86,19 +89,29 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // Two floats to two bf16 (round to nearest even), low half first.
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// a1: index decode + compaction.  The list is read in groups of EG rounds of
-// NT entries: every thread loads its (up to) EG entries of a group at once
-// (one memory round trip), a ballot per round gives each valid entry its
+// Two floats to two fp16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+}
+
+__device__ __forceinline__ f32x2_t unpack2_f16(uint32_t w) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+}
+
+// a1: index decode + compaction of a list already staged in LDS.  The list
+// is read in groups of EG rounds of NT entries: every thread reads its (up
+// to) EG entries of a group, a ballot per round gives each valid entry its
 // slot, and one barrier publishes the per-wave counts.  Entries keep their
 // order.  Returns the number of valid entries (0 <= idx < N).
 template <int NT>
-__device__ int compact_list(const int32_t *__restrict__ lst, int K, int64_t N, int32_t *list,
+__device__ int compact_list(const LDS_AS int32_t *lst, int K, int64_t N, int32_t *list,
                             int32_t *cnt /* [EG][NT/64] */) {
     constexpr int NWV = NT / 64;
     constexpr int EG = 8;
@@ -145,6 +158,15 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, const LDS_AS void *l
     // the LDS base is wave-uniform; readfirstlane puts it in an SGPR for M0
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(m0)
+                 : "memory", "m0");
+}
+
+// Same with 4 bytes per lane (landing at lds_base + 4 * lane).
+__device__ __forceinline__ void lds_dma4(const void *gptr, const LDS_AS void *lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(gptr), "s"(m0)
                  : "memory", "m0");
@@ -206,32 +228,58 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     const int g = lane >> 4;      // 16-lane block of the wave
     const int li = lane & 15;
 
-    // a3: this lane's head and its half of the query row, held as MFMA B
-    // operands: qf[k] = q[h, 32kk + 8g .. 32kk + 8g + 7] with kk = dh*DSH + k.
-    // Issued before the list loads: the wait for the list then covers q too,
-    // so the chunk loop never waits on q behind the row DMAs.
     const int h = hg * (NHQ * 16) + hq * 16 + li;
     const bool h_ok = h < p.H;
-    bf16x8_t qf[DSH];
+    const uint16_t *kvb = p.kv + (int64_t)b * p.N * D;
+    static_assert(NBUF == 4, "the prologue stages q in ring slots 1-2 and the list in slot 3");
+
+    // Prologue.  The index list and q come in through LDS-DMA too, so every
+    // wait of the prologue and the ring is one of ours and the first row
+    // chunk is requested as soon as the list is compacted.  Per wave, in
+    // issue order: its share of the raw list (4 bytes per lane, into slot 3),
+    // its q block (QIW instructions, into slots 1-2), chunk 0, then chunks
+    // 1 and 2 once q has been read out of slots 1-2.
+    LDS_AS int32_t *raw = (LDS_AS int32_t *)&tile[3][0];
     {
-        const uint16_t *qrow = p.q + ((int64_t)qi * p.H + (h_ok ? h : 0)) * D + dh * (D / 2);
-#pragma unroll
-        for (int k = 0; k < DSH; ++k)
-            qf[k] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(qrow + 32 * k + 8 * g));
+        const int32_t *lst = p.idxs + (int64_t)qi * p.K;
+        const int NI = (p.K + 63) / 64;
+        for (int i = wid; i < NI; i += NW) {
+            const int k = i * 64 + lane;
+            if (k < p.K) lds_dma4(lst + k, raw + i * 64);
+        }
     }
+    // a3: this wave's 16 heads x D/2 of q: head row hh of the block is D
+    // bytes at qstage + hh*D; its 16-byte chunk c sits at c ^ qswz(hh).
+    constexpr int QC = D / 16;                   // 16-byte chunks per half row
+    constexpr int HPI = 64 / QC;                 // half rows per DMA instruction
+    constexpr int QIW = 16 / HPI;                // q DMA instructions per wave
+    auto qswz = [](int hh) {
+        return QC >= 32 ? (2 * hh) & 31 : (2 * (hh / (32 / QC))) & (QC - 1);
+    };
+    LDS_AS uint8_t *qstage = (LDS_AS uint8_t *)&tile[1][0] + wid * (16 * D);
+    {
+        const int hbq = hg * (NHQ * 16) + hq * 16;
+#pragma unroll
+        for (int k = 0; k < QIW; ++k) {
+            const int hh = k * HPI + lane / QC;
+            const int pos = lane % QC;
+            // heads beyond H read head 0 (in bounds); their q is zeroed below.
+            // Every wave issues exactly QIW instructions: the waits count them.
+            const int hsrc = hbq + hh < p.H ? hbq + hh : 0;
+            const uint16_t *src = p.q + ((int64_t)qi * p.H + hsrc) * D + dh * (D / 2) +
+                                  ((pos ^ qswz(hh)) << 3);
+            lds_dma16(src, qstage + k * 1024);
+        }
+    }
+    // the raw list of this wave has landed once only its q DMAs are pending
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QIW) : "memory");
+    __syncthreads();
 
     // a1: decode and compact the list, then take this split's slice.
-    const int n = compact_list<NT>(p.idxs + (int64_t)qi * p.K, p.K, p.N, list, cnt);
-    // q has landed before the row ring starts (the list wait usually covers it
-    // already).  This wait is the compiler-visible form, so the compiler does
-    // not place waits for q inside the chunk loop, where they would also wait
-    // for the row DMAs in flight.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
+    const int n = compact_list<NT>(raw, p.K, p.N, list, cnt);
     const int lo = (int)(((int64_t)n * s) / p.S);
     const int hi = (int)(((int64_t)n * (s + 1)) / p.S);
     const int nchunks = (hi - lo + KC - 1) / KC;
-
-    const uint16_t *kvb = p.kv + (int64_t)b * p.N * D;
 
     // a2: gather the rows of chunk c into ring slot c % NBUF with LDS-DMA.
     // Each wave instruction moves RPI whole rows: lane l lands at byte 16*l of
@@ -253,23 +301,28 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             lds_dma16(src, dst);
         }
     };
-#pragma unroll
-    for (int c = 0; c < NBUF - 1; ++c)
-        if (c < nchunks) stage(c);
+    if (nchunks > 0) stage(0);
 
-    if (!h_ok) {
+    // q of this wave has landed once only chunk 0 is pending; move it to the
+    // MFMA B operands qf[k] = q[h, dh*D/2 + 32k + 8g .. +7] (zero for heads
+    // beyond H), then free slots 1-2 for chunks 1 and 2.
+    if (nchunks > 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    bf16x8_t qf[DSH];
 #pragma unroll
-        for (int k = 0; k < DSH; ++k) qf[k] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+    for (int k = 0; k < DSH; ++k) {
+        const int c = 4 * k + g;
+        u32x4_t v = *(const LDS_AS u32x4_t *)(qstage + li * D + ((c ^ qswz(li)) << 4));
+        if (!h_ok) v = u32x4_t{0, 0, 0, 0};
+        qf[k] = __builtin_bit_cast(bf16x8_t, v);
     }
+    __syncthreads();
+    if (1 < nchunks) stage(1);
+    if (2 < nchunks) stage(2);
 
     // Softmax state of head h (log2 units), identical in both waves of the
-    // pair.  The non-split path starts from the sink: max = sink, denominator
-    // = 1 (counted once per wave, in block 0).
+    // pair.  The sink is folded in by the epilogue.
     float m = -INFINITY, lsum = 0.f;
-    if (p.S == 1 && p.sink != nullptr && h_ok) {
-        m = p.sink[h] * LOG2E;
-        lsum = g == 0 ? 1.f : 0.f;
-    }
     f32x4_t o[DTH];
 #pragma unroll
     for (int t = 0; t < DTH; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -376,7 +429,14 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     // store instruction on distinct banks.
     float ltot = lsum + shfl_xor_f(lsum, 16);
     ltot += shfl_xor_f(ltot, 32);
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (p.S == 1 && p.sink != nullptr && h_ok) {
+        // the sink joins the softmax: M = max(m, sink), L = l 2^(m-M) + 2^(sink-M)
+        const float zs = p.sink[h] * LOG2E;
+        const float M = fmaxf(m, zs);
+        const float alpha = m == -INFINITY ? 0.f : exp2_fast(m - M);
+        inv = alpha / (ltot * alpha + exp2_fast(zs - M));
+    }
     __syncthreads();  // every wave is done with the ring; reuse it for staging
     LDS_AS uint8_t *stage_out = (LDS_AS uint8_t *)&tile[0][0];
     const int hl = hq * 16 + li;  // head row within the workgroup
@@ -402,40 +462,58 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
                 *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v;
         }
     } else {
-        constexpr int C32 = D / 4;  // 16-byte chunks per float32 row
-        static_assert(NHQ * 16 * D * 4 <= NBUF * KC * ROWB, "float32 staging fits in the ring");
-        LDS_AS uint8_t *Rrow = stage_out + hl * (D * 4);
+        // A split's partial: fp16 rows (11 significant bits) scaled by a power
+        // of two per (head, half row) so that |value| < 2^15 never overflows.
+        float amax = 0.f;
+#pragma unroll
+        for (int t = 0; t < DTH; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[t][i] * inv));
+        amax = fmaxf(amax, shfl_xor_f(amax, 16));
+        amax = fmaxf(amax, shfl_xor_f(amax, 32));
+        int ex = 0;
+        if (amax < INFINITY) (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1)
+        const int e = ex > 15 ? ex - 15 : 0;
+        const float down = ldexpf(inv, -e);
+        constexpr int C16 = D / 8;  // 16-byte chunks per 16-bit row
+        LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
 #pragma unroll
         for (int t = 0; t < DTH; ++t) {
             const int col = dh * (D / 2) + 16 * t + 4 * g;
-            const int pos = (col >> 2) ^ swz<C32>(hl);
-            *(LDS_AS f32x4_t *)(Rrow + pos * 16) = o[t] * inv;
+            const int pos = (col >> 3) ^ swz<C16>(hl);
+            const u32x2_t w = {pack2_f16(o[t][0] * down, o[t][1] * down),
+                               pack2_f16(o[t][2] * down, o[t][3] * down)};
+            *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
         }
-        if (g == 0 && dh == 0 && h_ok) {
+        if (g == 0 && h_ok) {
             const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
-            p.ws_m[slot] = m;
-            p.ws_l[slot] = ltot;
+            p.ws_x[slot * 2 + dh] = ldexpf(1.f, e);
+            if (dh == 0) {
+                p.ws_m[slot] = m;
+                p.ws_l[slot] = ltot;
+            }
         }
         __syncthreads();
-        float *dst = p.ws_o + ((int64_t)qi * p.S + s) * p.H * D;
-        for (int i = tid; i < NHQ * 16 * C32; i += NT) {
-            const int r = i / C32, pos = i % C32;
-            const f32x4_t v = *(const LDS_AS f32x4_t *)(stage_out + r * (D * 4) + pos * 16);
+        uint16_t *dst = p.ws_o + ((int64_t)qi * p.S + s) * p.H * D;
+        for (int i = tid; i < NHQ * 16 * C16; i += NT) {
+            const int r = i / C16, pos = i % C16;
+            const u32x4_t v = *(const LDS_AS u32x4_t *)(stage_out + r * (D * 2) + pos * 16);
             if (hbase + r < p.H)
-                *(f32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C32>(r)) << 2)) = v;
+                *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v;
         }
     }
 }
 
 // a9: log-sum-exp merge of the splits.  Split s holds p_s (its output
-// normalised by its own denominator l_s, float32), its max m_s and l_s (log2
-// units).  With M = max(sink, max_s m_s) and
-// L = 2^(sink - M) + sum_s 2^(m_s - M) l_s, out = sum_s (2^(m_s - M) l_s / L) p_s.
-// One wave per (query, head) row when D = 512; each lane merges 8 columns.
+// normalised by its own denominator l_s; fp16 times the power of two x_s of
+// the half row), its max m_s and l_s (log2 units).  With
+// M = max(sink, max_s m_s) and L = 2^(sink - M) + sum_s 2^(m_s - M) l_s,
+// out = sum_s (2^(m_s - M) l_s / L) p_s.  One lane merges 8 columns.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ws_o,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ ws_o,
                                                       const float *__restrict__ ws_m,
                                                       const float *__restrict__ ws_l,
+                                                      const float *__restrict__ ws_x,
                                                       const float *__restrict__ sink,
                                                       uint16_t *__restrict__ out, int64_t QH,
                                                       int H, int S) {
@@ -444,12 +522,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     if (idx >= QH * LPR) return;
     const int64_t qh = idx / LPR;
     const int c8 = (int)(idx % LPR) * 8;
+    const int half = c8 >= D / 2 ? 1 : 0;
     const int64_t qi = qh / H;
     const int h = (int)(qh % H);
     const float mz = sink != nullptr ? sink[h] * LOG2E : -INFINITY;
     float mx = mz;
     for (int s = 0; s < S; ++s) mx = fmaxf(mx, ws_m[(qi * S + s) * H + h]);
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (mx != -INFINITY) {
         float L = sink != nullptr ? exp2_fast(mz - mx) : 0.f;
         for (int s = 0; s < S; ++s)
@@ -457,13 +536,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         const float invL = L > 0.f ? 1.f / L : 0.f;
         for (int s = 0; s < S; ++s) {
             const int64_t slot = (qi * S + s) * H + h;
-            const float c = exp2_fast(ws_m[slot] - mx) * ws_l[slot] * invL;
-            a0 += c * *(const f32x4_t *)(ws_o + slot * D + c8);
-            a1 += c * *(const f32x4_t *)(ws_o + slot * D + c8 + 4);
+            const float c = exp2_fast(ws_m[slot] - mx) * ws_l[slot] * invL * ws_x[slot * 2 + half];
+            const u32x4_t v = *(const u32x4_t *)(ws_o + slot * D + c8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f32x2_t f = unpack2_f16(v[e]);
+                acc[2 * e] += c * f[0];
+                acc[2 * e + 1] += c * f[1];
+            }
         }
     }
-    const u32x4_t w = {pack2_bf16(a0[0], a0[1]), pack2_bf16(a0[2], a0[3]),
-                       pack2_bf16(a1[0], a1[1]), pack2_bf16(a1[2], a1[3])};
+    const u32x4_t w = {pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]),
+                       pack2_bf16(acc[4], acc[5]), pack2_bf16(acc[6], acc[7])};
     *(u32x4_t *)(out + qh * D + c8) = w;
 }
 
@@ -513,18 +597,19 @@ bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) =
 int64_t queries(const sa_dims *d) { return (int64_t)d->B * d->T; }
 
 struct WsLayout {
-    size_t o_off, m_off, l_off, bytes;
+    size_t o_off, m_off, l_off, x_off, bytes;
 };
 
 WsLayout ws_layout(const sa_dims *d, int S) {
-    WsLayout w{0, 0, 0, 0};
+    WsLayout w{0, 0, 0, 0, 0};
     if (S <= 1) return w;
     const size_t slots = (size_t)queries(d) * S * d->H;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     w.o_off = 0;
-    w.m_off = up(slots * d->D * sizeof(float));
+    w.m_off = up(slots * d->D * sizeof(uint16_t));
     w.l_off = w.m_off + up(slots * sizeof(float));
-    w.bytes = w.l_off + up(slots * sizeof(float));
+    w.x_off = w.l_off + up(slots * sizeof(float));
+    w.bytes = w.x_off + up(slots * 2 * sizeof(float));
     return w;
 }
 
@@ -563,14 +648,15 @@ hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
     const int64_t QH = queries(d) * d->H;
     const int64_t threads = QH * (d->D / 8);
     const unsigned grid = (unsigned)((threads + 255) / 256);
-    const float *wo = (const float *)((const uint8_t *)ws + L.o_off);
+    const uint16_t *wo = (const uint16_t *)((const uint8_t *)ws + L.o_off);
     const float *wm = (const float *)((const uint8_t *)ws + L.m_off);
     const float *wl = (const float *)((const uint8_t *)ws + L.l_off);
+    const float *wx = (const float *)((const uint8_t *)ws + L.x_off);
     uint16_t *o = (uint16_t *)out;
     switch (d->D) {
-        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, sink, o, QH, d->H, S); break;
-        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, sink, o, QH, d->H, S); break;
-        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, sink, o, QH, d->H, S); break;
+        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S); break;
+        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S); break;
+        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S); break;
     }
     return hipGetLastError();
 }
@@ -616,9 +702,10 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
     p.out = (uint16_t *)out;
     const WsLayout L = ws_layout(d, S);
     if (S > 1) {
-        p.ws_o = (float *)((uint8_t *)ws + L.o_off);
+        p.ws_o = (uint16_t *)((uint8_t *)ws + L.o_off);
         p.ws_m = (float *)((uint8_t *)ws + L.m_off);
         p.ws_l = (float *)((uint8_t *)ws + L.l_off);
+        p.ws_x = (float *)((uint8_t *)ws + L.x_off);
     }
     p.N = d->N;
     p.T = d->T;

@@ -108,7 +108,7 @@ def test_workspace_size_formula(L):
     got = L.sparse_attn_workspace_bytes(dims(B=B, T=T, H=H, D=D), S)
     up = lambda x: (x + 255) // 256 * 256
     slots = B * T * S * H
-    assert got == up(slots * D * 4) + 2 * up(slots * 4)
+    assert got == up(slots * D * 2) + 2 * up(slots * 4) + up(slots * 8)
     assert L.sparse_attn_workspace_bytes(dims(), 1) == 0
     assert L.sparse_attn_workspace_bytes(dims(D=100), 2) == 0
 

@@ -126,6 +126,23 @@ def test_large_norm_queries(ref):
         check(ref, w, S, q_bits=q8, what=f"8x query S={S}")
 
 
+def test_large_magnitude_rows_on_the_split_path(ref):
+    # rows ~2^20: a split's partial output would overflow fp16 without the
+    # per-half-row power-of-two scale
+    import copy
+    w = copy.deepcopy(wl.make_random(15, 2, 2, 64, 512, 300, 200, p_unused=0.1))
+    w.vals = [wl.to_bf16_bits(wl.bf16_bits_to_f32(v) * np.float32(2.0 ** 20)) for v in w.vals]
+    # q scaled down by the same power of two keeps the scores (and the softmax)
+    # as in the unscaled case, so the outputs are ~2^20 times a typical output
+    q_small = wl.to_bf16_bits(wl.bf16_bits_to_f32(w.q) * np.float32(2.0 ** -20))
+    exp = ref(q_small, w.kv_host(), w.sink, w.idxs, w.scale)
+    assert np.abs(exp).max() > 65504.0   # beyond fp16 without the scale
+    for S in (1, 2, 3):
+        got = run_gpu(w, S, q_bits=q_small)
+        # the output is linear in the rows: compare at the unscaled magnitude
+        assert_close(got * 2.0 ** -20, exp * 2.0 ** -20, f"rows x 2^20 S={S}")
+
+
 def test_permuted_lists_and_scattered_unused(ref):
     w = wl.make_random(11, 2, 2, 64, 512, 400, 300, p_unused=0.3)
     rng = np.random.default_rng(0)
