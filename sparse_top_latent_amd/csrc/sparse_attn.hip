@@ -359,23 +359,27 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         sacc[0] += xpeer[0];
         sacc[1] += xpeer[64];
 
-        // a5: mask + online sink-softmax.  Lane (li, g) holds rows
-        // j = 16 jt + 4 g + i of head h.
+        // a5: mask + online softmax.  Lane (li, g) holds rows j = 16 jt + 4 g + i
+        // of head h.  The kept max m only moves when a score beats it by more
+        // than MAX_SLACK; a per-lane check and one ballot decide that, and the
+        // exact chunk max (two cross-lane reductions) is only taken then.
         float sv[8];
-        float cmax = -INFINITY;
+        if (cnt_c == KC) {
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+            for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3] * p.qk_scale_log2;
+        } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 16 * jt + 4 * g + i;
-                const float x = j < cnt_c ? sacc[jt][i] * p.qk_scale_log2 : -INFINITY;
-                sv[jt * 4 + i] = x;
-                cmax = fmaxf(cmax, x);
+            for (int e = 0; e < 8; ++e) {
+                const int j = 16 * (e >> 2) + 4 * g + (e & 3);
+                sv[e] = j < cnt_c ? sacc[e >> 2][e & 3] * p.qk_scale_log2 : -INFINITY;
             }
-        cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
-        cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
-        const bool raise = cmax > m + MAX_SLACK;
-        if (__ballot(raise)) {
+        }
+        float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                           fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        if (__ballot(lmax > m + MAX_SLACK)) {
+            float cmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
+            cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+            const bool raise = cmax > m + MAX_SLACK;
             const float mnew = raise ? cmax : m;
             const float alpha = exp2_fast(m - mnew);
             lsum *= alpha;
