@@ -66,16 +66,13 @@ struct FwdParams {
     float qk_scale_log2;  // scale * log2(e)
 };
 
-// Row swizzle of the 16-byte chunks inside a row of the LDS tile: chunk c of
-// row r lives at position c ^ swz<CPR>(r).  gfx950's LDS serves a b128 read
-// 32 lanes (512 bytes) per pass, so the 32 lanes of a half-wave must land in
-// 32 distinct 16-byte bank slots (slot = byte address / 16 mod 32).  The
-// operand load of QK^T has lanes (row li, chunk c0 or c0^1): an even swizzle
-// keeps the two chunk parities apart and spreads the 16 rows.  Rows of 1 KB
-// or 512 B all start on slot 0, so swz = 2r mod 32; 256-byte rows alternate
-// between slot 0 and 16, so the rows of one parity share 2*(r/2) mod 16.  The
-// transpose loads of PV (rows 4g + i/4, chunk pairs 2t, 2t+1) are spread by
-// the same swizzle.  Rows r and r + 16 share a swizzle.
+// Row swizzle of the 16-byte chunks of a 16-bit row in an LDS staging area
+// (the epilogue's output rows): chunk c of row r lives at position
+// c ^ swz<CPR>(r).  gfx950's LDS serves a b128 access 32 lanes (512 bytes)
+// per pass, so the 32 lanes of a half-wave must land in 32 distinct 16-byte
+// bank slots (slot = byte address / 16 mod 32).  Rows of 1 KB or 512 B all
+// start on slot 0, so swz = 2r mod 32; 256-byte rows alternate between slot
+// 0 and 16, so the rows of one parity share 2*(r/2) mod 16.
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
     return CPR >= 32 ? (2 * r) & 31 : (2 * (r >> 1)) & 15;
@@ -183,32 +180,41 @@ __device__ __forceinline__ void wait_vm_ahead(int ahead) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Work split: a workgroup holds NHQ groups of 16 heads; each group is served
-// by a pair of waves, one per half of the head dimension.  For QK^T a wave
-// sums over its half of d and the pair adds the two partial scores through
-// LDS, so both waves of the pair hold the same scores and run the same
+// Work split: a workgroup holds NHQ groups of 16*HT heads; each group is
+// served by a pair of waves, one per half of the head dimension.  For QK^T a
+// wave sums over its half of d and the pair adds the two partial scores
+// through LDS, so both waves of the pair hold the same scores and run the same
 // softmax; for PV each wave produces its half of the output columns.  A wave
-// therefore keeps only 16 x D/2 accumulators and 16 x D/2 query values in
-// registers, which leaves room for two waves per SIMD.
-template <int D, int NHQ>
+// holds HT tiles of 16 heads: every K or V operand it reads from LDS feeds HT
+// MFMAs, so LDS read traffic per chunk falls as 1/HT, at the cost of HT x
+// (16 x D/2) accumulators and query values in registers.
+template <int D, int NHQ, int HT>
 __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     constexpr int NW = 2 * NHQ;            // waves per workgroup
     constexpr int NT = NW * 64;
+    constexpr int HW = 16 * HT;            // heads per wave
+    constexpr int HWG = NHQ * HW;          // heads per workgroup
     constexpr int ROWB = D * 2;            // bytes per row
     constexpr int CPR = D / 8;             // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;          // rows per LDS-DMA wave instruction
-    constexpr int NINS = KC / RPI;         // DMA wave instructions per chunk
-    constexpr int IPW = NINS / NW;         // ... per wave
+    // Ring rows are padded to RS bytes: with RS = 2D + 32 the 16-byte slot of
+    // row r, chunk c is (r (D/8 + 2) + c) mod 32, and 2(D/8 + 2) mod 32 keeps
+    // rows apart, so the QK^T operand loads (16 rows x two chunk parities per
+    // half-wave) and the PV transpose loads (16 rows x 4 eight-byte words per
+    // wave) are free of bank conflicts with affine addresses (immediate
+    // offsets, no per-load address arithmetic).
+    constexpr int RS = ROWB + 32;          // LDS bytes per ring row
+    constexpr int IPW = KC / NW;           // DMA wave instructions (one row each) per wave
     constexpr int DSH = D / 64;            // MFMA k-steps over one half of d
     constexpr int DTH = D / 32;            // 16-wide output tiles in one half of d
     // LDS ring depth (chunks): up to 4, as long as the DMA instructions of the
     // chunks in flight fit the 6-bit vmcnt
     constexpr int NBUF = 2 + (63 / IPW >= 2 ? 2 : 63 / IPW);
     static_assert(CPR >= 16 && 64 % CPR == 0, "row swizzle needs D in {128, 256, 512}");
-    static_assert(NINS % NW == 0, "DMA instructions must split evenly over the waves");
+    static_assert(KC % NW == 0, "DMA instructions must split evenly over the waves");
+    static_assert(HT == 1 || HT == 2, "one or two head tiles per wave");
 
-    __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][KC * ROWB];
-    __shared__ __attribute__((aligned(16))) f32x4_t xbuf[NW][2][64];  // partial scores
+    __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][KC * RS];
+    __shared__ __attribute__((aligned(16))) f32x4_t xbuf[NW][2 * HT][64];  // partial scores
     __shared__ int32_t list[LIST_CAP];
     __shared__ int32_t cnt[8 * NW];
 
@@ -228,8 +234,8 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     const int g = lane >> 4;      // 16-lane block of the wave
     const int li = lane & 15;
 
-    const int h = hg * (NHQ * 16) + hq * 16 + li;
-    const bool h_ok = h < p.H;
+    // head of this lane in head tile t: hw0 + 16 t + li
+    const int hw0 = hg * HWG + hq * HW;
     const uint16_t *kvb = p.kv + (int64_t)b * p.N * D;
     static_assert(NBUF == 4, "the prologue stages q in ring slots 1-2 and the list in slot 3");
 
@@ -248,24 +254,24 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             if (k < p.K) lds_dma4(lst + k, raw + i * 64);
         }
     }
-    // a3: this wave's 16 heads x D/2 of q: head row hh of the block is D
+    // a3: this wave's HW heads x D/2 of q: head row hh of the block is D
     // bytes at qstage + hh*D; its 16-byte chunk c sits at c ^ qswz(hh).
     constexpr int QC = D / 16;                   // 16-byte chunks per half row
     constexpr int HPI = 64 / QC;                 // half rows per DMA instruction
-    constexpr int QIW = 16 / HPI;                // q DMA instructions per wave
+    constexpr int QIW = HW / HPI;                // q DMA instructions per wave
+    static_assert(NW * HW * D <= 2 * KC * RS, "q of the workgroup fits ring slots 1-2");
     auto qswz = [](int hh) {
         return QC >= 32 ? (2 * hh) & 31 : (2 * (hh / (32 / QC))) & (QC - 1);
     };
-    LDS_AS uint8_t *qstage = (LDS_AS uint8_t *)&tile[1][0] + wid * (16 * D);
+    LDS_AS uint8_t *qstage = (LDS_AS uint8_t *)&tile[1][0] + wid * (HW * D);
     {
-        const int hbq = hg * (NHQ * 16) + hq * 16;
 #pragma unroll
         for (int k = 0; k < QIW; ++k) {
             const int hh = k * HPI + lane / QC;
             const int pos = lane % QC;
             // heads beyond H read head 0 (in bounds); their q is zeroed below.
             // Every wave issues exactly QIW instructions: the waits count them.
-            const int hsrc = hbq + hh < p.H ? hbq + hh : 0;
+            const int hsrc = hw0 + hh < p.H ? hw0 + hh : 0;
             const uint16_t *src = p.q + ((int64_t)qi * p.H + hsrc) * D + dh * (D / 2) +
                                   ((pos ^ qswz(hh)) << 3);
             lds_dma16(src, qstage + k * 1024);
@@ -282,50 +288,64 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     const int nchunks = (hi - lo + KC - 1) / KC;
 
     // a2: gather the rows of chunk c into ring slot c % NBUF with LDS-DMA.
-    // Each wave instruction moves RPI whole rows: lane l lands at byte 16*l of
-    // the instruction's 1 KB, i.e. row r = l / CPR at position l % CPR, so it
-    // fetches the row's chunk (position ^ swz(r)).  Tail slots repeat the
-    // chunk's first row; their scores are masked to -inf below.
+    // Each wave instruction moves one row: lane l < D/8 fetches its 16 bytes
+    // and lands at byte 16*l of the row's padded slot.  Tail slots repeat the
+    // chunk's first row; their scores are masked to -inf below.  All row
+    // numbers are read from the list before the first DMA is issued: the DMA
+    // asm orders memory, so interleaving them would put one LDS round trip in
+    // front of every DMA.
     auto stage = [&](int c) {
         const int e0 = lo + c * KC;
         uint8_t *buf = &tile[c % NBUF][0];
+        int row[IPW];
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
-            const int ii = k * NW + wid;
-            const int r = ii * RPI + lane / CPR;
-            const int pos = lane % CPR;
-            const int e = e0 + r;
-            const int row = list[e < hi ? e : e0];
-            const uint16_t *src = kvb + (int64_t)row * D + ((pos ^ swz<CPR>(r)) << 3);
-            LDS_AS void *dst = (LDS_AS void *)((LDS_AS uint8_t *)buf + ii * 1024);
-            lds_dma16(src, dst);
+            const int e = e0 + k * NW + wid;
+            row[k] = list[e < hi ? e : e0];
+        }
+#pragma unroll
+        for (int k = 0; k < IPW; ++k) {
+            const int r = k * NW + wid;
+            if (CPR == 64 || lane < CPR)
+                lds_dma16(kvb + (int64_t)row[k] * D + lane * 8,
+                          (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS));
         }
     };
     if (nchunks > 0) stage(0);
 
     // q of this wave has landed once only chunk 0 is pending; move it to the
-    // MFMA B operands qf[k] = q[h, dh*D/2 + 32k + 8g .. +7] (zero for heads
-    // beyond H), then free slots 1-2 for chunks 1 and 2.
+    // MFMA B operands qf[t][k] = q[hw0 + 16t + li, dh*D/2 + 32k + 8g .. +7]
+    // (zero for heads beyond H), then free slots 1-2 for chunks 1 and 2.
     if (nchunks > 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    bf16x8_t qf[DSH];
+    bf16x8_t qf[HT][DSH];
 #pragma unroll
-    for (int k = 0; k < DSH; ++k) {
-        const int c = 4 * k + g;
-        u32x4_t v = *(const LDS_AS u32x4_t *)(qstage + li * D + ((c ^ qswz(li)) << 4));
-        if (!h_ok) v = u32x4_t{0, 0, 0, 0};
-        qf[k] = __builtin_bit_cast(bf16x8_t, v);
+    for (int t = 0; t < HT; ++t) {
+        const int hh = 16 * t + li;
+        const bool ok = hw0 + hh < p.H;
+#pragma unroll
+        for (int k = 0; k < DSH; ++k) {
+            const int c = 4 * k + g;
+            u32x4_t v = *(const LDS_AS u32x4_t *)(qstage + hh * D + ((c ^ qswz(hh)) << 4));
+            if (!ok) v = u32x4_t{0, 0, 0, 0};
+            qf[t][k] = __builtin_bit_cast(bf16x8_t, v);
+        }
     }
     __syncthreads();
     if (1 < nchunks) stage(1);
     if (2 < nchunks) stage(2);
 
-    // Softmax state of head h (log2 units), identical in both waves of the
-    // pair.  The sink is folded in by the epilogue.
-    float m = -INFINITY, lsum = 0.f;
-    f32x4_t o[DTH];
+    // Softmax state of head hw0 + 16t + li (log2 units), identical in both
+    // waves of the pair.  The sink is folded in by the epilogue.
+    float m[HT], lsum[HT];
+    f32x4_t o[HT][DTH];
 #pragma unroll
-    for (int t = 0; t < DTH; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < HT; ++t) {
+        m[t] = -INFINITY;
+        lsum[t] = 0.f;
+#pragma unroll
+        for (int u = 0; u < DTH; ++u) o[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     LDS_AS f32x4_t *xmine = (LDS_AS f32x4_t *)&xbuf[wid][0][lane];
     const LDS_AS f32x4_t *xpeer = (const LDS_AS f32x4_t *)&xbuf[wid ^ 1][0][lane];
@@ -339,172 +359,186 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NBUF][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
 
-        // a4: partial S^T[j, h] over this wave's half of d (two 16-row tiles).
-        f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        // a4: partial S^T[j, h] over this wave's half of d (two 16-row tiles
+        // x HT head tiles; each K operand feeds HT MFMAs).
+        f32x4_t sacc[2][HT];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int t = 0; t < HT; ++t) sacc[jt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < DSH; ++k) {
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
                 const int r = jt * 16 + li;
-                const int pos = (4 * (dh * DSH + k) + g) ^ swz<CPR>(r);
-                const u32x4_t a = *(const LDS_AS u32x4_t *)(T + r * ROWB + pos * 16);
-                sacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, a), qf[k], sacc[jt], 0, 0, 0);
+                const int pos = 4 * (dh * DSH + k) + g;
+                const bf16x8_t a = __builtin_bit_cast(
+                    bf16x8_t, *(const LDS_AS u32x4_t *)(T + r * RS + pos * 16));
+#pragma unroll
+                for (int t = 0; t < HT; ++t)
+                    sacc[jt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[t][k], sacc[jt][t], 0, 0, 0);
             }
         }
         // the pair adds its two halves (a + b == b + a, so both waves agree)
-        xmine[0] = sacc[0];
-        xmine[64] = sacc[1];
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+            xmine[(2 * t) * 64] = sacc[0][t];
+            xmine[(2 * t + 1) * 64] = sacc[1][t];
+        }
         __syncthreads();
-        sacc[0] += xpeer[0];
-        sacc[1] += xpeer[64];
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+            sacc[0][t] += xpeer[(2 * t) * 64];
+            sacc[1][t] += xpeer[(2 * t + 1) * 64];
+        }
 
         // a5: mask + online softmax.  Lane (li, g) holds rows j = 16 jt + 4 g + i
-        // of head h.  The kept max m only moves when a score beats it by more
-        // than MAX_SLACK; a per-lane check and one ballot decide that, and the
-        // exact chunk max (two cross-lane reductions) is only taken then.
-        float sv[8];
-        if (cnt_c == KC) {
+        // of head tile t.  The kept max m only moves when a score beats it by
+        // more than MAX_SLACK; a per-lane check and one ballot decide that, and
+        // the exact chunk max (two cross-lane reductions) is only taken then.
+        bf16x8_t pb[HT];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3] * p.qk_scale_log2;
-        } else {
+        for (int t = 0; t < HT; ++t) {
+            float sv[8];
+            if (cnt_c == KC) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = 16 * (e >> 2) + 4 * g + (e & 3);
-                sv[e] = j < cnt_c ? sacc[e >> 2][e & 3] * p.qk_scale_log2 : -INFINITY;
+                for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][t][e & 3] * p.qk_scale_log2;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 16 * (e >> 2) + 4 * g + (e & 3);
+                    sv[e] = j < cnt_c ? sacc[e >> 2][t][e & 3] * p.qk_scale_log2 : -INFINITY;
+                }
             }
+            float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                               fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            if (__ballot(lmax > m[t] + MAX_SLACK)) {
+                float cmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
+                cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+                const bool raise = cmax > m[t] + MAX_SLACK;
+                const float mnew = raise ? cmax : m[t];
+                const float alpha = exp2_fast(m[t] - mnew);
+                lsum[t] *= alpha;
+#pragma unroll
+                for (int u = 0; u < DTH; ++u) o[t][u] *= alpha;
+                m[t] = mnew;
+            }
+            // The weights enter the value product as bf16; the denominator sums
+            // the same rounded weights, so numerator and denominator agree.
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(sv[e] - m[t]);
+            const u32x4_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3]),
+                                pack2_bf16(pv[4], pv[5]), pack2_bf16(pv[6], pv[7])};
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                psum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
+            lsum[t] += psum;
+            pb[t] = __builtin_bit_cast(bf16x8_t, pw);
         }
-        float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                           fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        if (__ballot(lmax > m + MAX_SLACK)) {
-            float cmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
-            cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
-            const bool raise = cmax > m + MAX_SLACK;
-            const float mnew = raise ? cmax : m;
-            const float alpha = exp2_fast(m - mnew);
-            lsum *= alpha;
-#pragma unroll
-            for (int t = 0; t < DTH; ++t) o[t] *= alpha;
-            m = mnew;
-        }
-        // The weights enter the value product as bf16; the denominator sums
-        // the same rounded weights, so numerator and denominator agree.
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(sv[e] - m);
-        const u32x4_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3]),
-                            pack2_bf16(pv[4], pv[5]), pack2_bf16(pv[6], pv[7])};
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            psum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
-        lsum += psum;
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
 
         // a6: O^T[d, h] += V^T[d, j] P^T[j, h] for this wave's half of d.
         // A operand through transpose loads: lane i of block g addresses row
         // 4g + i/4 (and +16), columns 16t + 4(i%4) .. +3; the load hands lane i
         // column 16t + i of rows 4g..4g+3, matching the weight slots
-        // j = 4g + e and 16 + 4g + e.
+        // j = 4g + e and 16 + 4g + e.  Each V operand feeds HT MFMAs.
         {
             const int r0 = 4 * g + (li >> 2);
-            const int sw = swz<CPR>(r0);  // rows r0 and r0 + 16 share the swizzle
-            const int half = (li & 1) * 8;
-            const LDS_AS uint8_t *R0 = T + r0 * ROWB + half;
-            const LDS_AS uint8_t *R1 = R0 + 16 * ROWB;
+            const LDS_AS uint8_t *R0 = T + r0 * RS + (li & 3) * 8;
+            const LDS_AS uint8_t *R1 = R0 + 16 * RS;
 #pragma unroll
-            for (int t = 0; t < DTH; ++t) {
-                const int tt = dh * DTH + t;
-                const int pos = ((2 * tt + ((li >> 1) & 1)) ^ sw) * 16;
+            for (int u = 0; u < DTH; ++u) {
+                const int tt = dh * DTH + u;
+                const int pos = tt * 32;
                 const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R0 + pos));
                 const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R1 + pos));
                 const bf16x8_t a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[t], 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < HT; ++t)
+                    o[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[t], o[t][u], 0, 0, 0);
             }
         }
     }
 
-    // a7 / a8: epilogue.  Lane (li, g) holds O^T[dh*D/2 + 16t + 4g + i, h].
-    // Every output (final, or a split's partial) is normalised by its own
-    // denominator, then staged through the (now idle) LDS ring so that each
-    // wave instruction stores 1 KB of contiguous row: the final output as
-    // bf16, a split's partial as float32.  In LDS, 16-byte chunk c of head row
-    // hl sits at position c ^ swz(hl), which keeps the 16 rows written by one
-    // store instruction on distinct banks.
-    float ltot = lsum + shfl_xor_f(lsum, 16);
-    ltot += shfl_xor_f(ltot, 32);
-    float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (p.S == 1 && p.sink != nullptr && h_ok) {
-        // the sink joins the softmax: M = max(m, sink), L = l 2^(m-M) + 2^(sink-M)
-        const float zs = p.sink[h] * LOG2E;
-        const float M = fmaxf(m, zs);
-        const float alpha = m == -INFINITY ? 0.f : exp2_fast(m - M);
-        inv = alpha / (ltot * alpha + exp2_fast(zs - M));
-    }
+    // a7 / a8: epilogue.  Lane (li, g) holds O^T[dh*D/2 + 16u + 4g + i, h] of
+    // head tile t.  Every output (final, or a split's partial) is normalised
+    // by its own denominator, then staged through the (now idle) LDS ring so
+    // that each wave instruction stores 1 KB of contiguous rows: the final
+    // output as bf16, a split's partial as fp16 scaled by a power of two.  In
+    // LDS, 16-byte chunk c of head row hl sits at position c ^ swz(hl), which
+    // keeps the 16 rows written by one store instruction on distinct banks.
     __syncthreads();  // every wave is done with the ring; reuse it for staging
     LDS_AS uint8_t *stage_out = (LDS_AS uint8_t *)&tile[0][0];
-    const int hl = hq * 16 + li;  // head row within the workgroup
-    const int hbase = hg * (NHQ * 16);
-    if (p.S == 1) {
-        constexpr int C16 = D / 8;  // 16-byte chunks per bf16 row
-        static_assert(NHQ * 16 * D * 2 <= NBUF * KC * ROWB, "bf16 staging fits in the ring");
+    const int hbase = hg * HWG;
+    constexpr int C16 = D / 8;  // 16-byte chunks per 16-bit row
+    static_assert(HWG * D * 2 <= NBUF * KC * RS, "staging fits in the ring");
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+        const int h = hw0 + 16 * t + li;
+        const bool h_ok = h < p.H;
+        const int hl = hq * HW + 16 * t + li;  // head row within the workgroup
+        float ltot = lsum[t] + shfl_xor_f(lsum[t], 16);
+        ltot += shfl_xor_f(ltot, 32);
+        float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
+        if (p.S == 1) {
+            if (p.sink != nullptr && h_ok) {
+                // the sink joins the softmax: M = max(m, sink), L = l 2^(m-M) + 2^(sink-M)
+                const float zs = p.sink[h] * LOG2E;
+                const float M = fmaxf(m[t], zs);
+                const float alpha = m[t] == -INFINITY ? 0.f : exp2_fast(m[t] - M);
+                inv = alpha / (ltot * alpha + exp2_fast(zs - M));
+            }
 #pragma unroll
-        for (int t = 0; t < DTH; ++t) {
-            const int col = dh * (D / 2) + 16 * t + 4 * g;  // first of 4 columns
-            const int pos = (col >> 3) ^ swz<C16>(hl);
-            const u32x2_t w = {pack2_bf16(o[t][0] * inv, o[t][1] * inv),
-                               pack2_bf16(o[t][2] * inv, o[t][3] * inv)};
-            *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
-        }
-        __syncthreads();
-        uint16_t *dst = p.out + (int64_t)qi * p.H * D;
-        for (int i = tid; i < NHQ * 16 * C16; i += NT) {
-            const int r = i / C16, pos = i % C16;
-            const u32x4_t v = *(const LDS_AS u32x4_t *)(stage_out + r * (D * 2) + pos * 16);
-            if (hbase + r < p.H)
-                *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v;
-        }
-    } else {
-        // A split's partial: fp16 rows (11 significant bits) scaled by a power
-        // of two per (head, half row) so that |value| < 2^15 never overflows.
-        float amax = 0.f;
+            for (int u = 0; u < DTH; ++u) {
+                const int col = dh * (D / 2) + 16 * u + 4 * g;  // first of 4 columns
+                const int pos = (col >> 3) ^ swz<C16>(hl);
+                const u32x2_t w = {pack2_bf16(o[t][u][0] * inv, o[t][u][1] * inv),
+                                   pack2_bf16(o[t][u][2] * inv, o[t][u][3] * inv)};
+                *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
+            }
+        } else {
+            // A split's partial: fp16 rows (11 significant bits) scaled by a
+            // power of two per (head, half row) so that |value| < 2^15 never
+            // overflows.
+            float amax = 0.f;
 #pragma unroll
-        for (int t = 0; t < DTH; ++t)
+            for (int u = 0; u < DTH; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[t][i] * inv));
-        amax = fmaxf(amax, shfl_xor_f(amax, 16));
-        amax = fmaxf(amax, shfl_xor_f(amax, 32));
-        int ex = 0;
-        if (amax < INFINITY) (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1)
-        const int e = ex > 15 ? ex - 15 : 0;
-        const float down = ldexpf(inv, -e);
-        constexpr int C16 = D / 8;  // 16-byte chunks per 16-bit row
-        LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
+                for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[t][u][i] * inv));
+            amax = fmaxf(amax, shfl_xor_f(amax, 16));
+            amax = fmaxf(amax, shfl_xor_f(amax, 32));
+            int ex = 0;
+            if (amax < INFINITY) (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1)
+            const int e = ex > 15 ? ex - 15 : 0;
+            const float down = ldexpf(inv, -e);
 #pragma unroll
-        for (int t = 0; t < DTH; ++t) {
-            const int col = dh * (D / 2) + 16 * t + 4 * g;
-            const int pos = (col >> 3) ^ swz<C16>(hl);
-            const u32x2_t w = {pack2_f16(o[t][0] * down, o[t][1] * down),
-                               pack2_f16(o[t][2] * down, o[t][3] * down)};
-            *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
-        }
-        if (g == 0 && h_ok) {
-            const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
-            p.ws_x[slot * 2 + dh] = ldexpf(1.f, e);
-            if (dh == 0) {
-                p.ws_m[slot] = m;
-                p.ws_l[slot] = ltot;
+            for (int u = 0; u < DTH; ++u) {
+                const int col = dh * (D / 2) + 16 * u + 4 * g;
+                const int pos = (col >> 3) ^ swz<C16>(hl);
+                const u32x2_t w = {pack2_f16(o[t][u][0] * down, o[t][u][1] * down),
+                                   pack2_f16(o[t][u][2] * down, o[t][u][3] * down)};
+                *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
+            }
+            if (g == 0 && h_ok) {
+                const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
+                p.ws_x[slot * 2 + dh] = ldexpf(1.f, e);
+                if (dh == 0) {
+                    p.ws_m[slot] = m[t];
+                    p.ws_l[slot] = ltot;
+                }
             }
         }
-        __syncthreads();
-        uint16_t *dst = p.ws_o + ((int64_t)qi * p.S + s) * p.H * D;
-        for (int i = tid; i < NHQ * 16 * C16; i += NT) {
-            const int r = i / C16, pos = i % C16;
-            const u32x4_t v = *(const LDS_AS u32x4_t *)(stage_out + r * (D * 2) + pos * 16);
-            if (hbase + r < p.H)
-                *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v;
-        }
+    }
+    __syncthreads();
+    uint16_t *dst = p.S == 1 ? p.out + (int64_t)qi * p.H * D
+                             : p.ws_o + ((int64_t)qi * p.S + s) * p.H * D;
+    for (int i = tid; i < HWG * C16; i += NT) {
+        const int r = i / C16, pos = i % C16;
+        const u32x4_t v = *(const LDS_AS u32x4_t *)(stage_out + r * (D * 2) + pos * 16);
+        if (hbase + r < p.H)
+            *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v;
     }
 }
 
@@ -512,7 +546,15 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 // normalised by its own denominator l_s; fp16 times the power of two x_s of
 // the half row), its max m_s and l_s (log2 units).  With
 // M = max(sink, max_s m_s) and L = 2^(sink - M) + sum_s 2^(m_s - M) l_s,
-// out = sum_s (2^(m_s - M) l_s / L) p_s.  One lane merges 8 columns.
+// out = sum_s (2^(m_s - M) l_s / L) p_s.
+//
+// LPR = D/8 lanes own one output row (8 columns each), so a wave merges
+// 64/LPR rows and a workgroup 4x that.  The first SB splits of the rows and
+// every (m, l, x) of the lane's row are requested before anything is waited
+// for, so the merge costs about one memory round trip.  The factors go through
+// a small LDS table (one per row).  Workgroups are laid out so that the rows
+// of a query are merged on the XCD whose workgroups wrote its partials (the
+// same blockIdx-to-XCD order as attn_fwd), where they may still sit in L2.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ ws_o,
                                                       const float *__restrict__ ws_m,
@@ -520,39 +562,97 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                                                       const float *__restrict__ ws_x,
                                                       const float *__restrict__ sink,
                                                       uint16_t *__restrict__ out, int64_t QH,
-                                                      int H, int S) {
-    constexpr int LPR = D / 8;  // lanes per row
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= QH * LPR) return;
-    const int64_t qh = idx / LPR;
-    const int c8 = (int)(idx % LPR) * 8;
+                                                      int H, int S, int per_xcd) {
+    constexpr int LPR = D / 8;       // lanes per row
+    constexpr int RPW = 64 / LPR;    // rows per wave
+    constexpr int RWG = 4 * RPW;     // rows per workgroup
+    constexpr int SB = 8;            // splits per batch of row loads
+    constexpr int SPL = MAX_SPLITS / LPR > 0 ? MAX_SPLITS / LPR : 1;  // scalar slots per lane
+    __shared__ f32x2_t coef[RWG][MAX_SPLITS];
+
+    const int bid = blockIdx.x;
+    const int64_t wg = (int64_t)(bid & 7) * per_xcd + (bid >> 3);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int rw = wid * RPW + lane / LPR;   // row within the workgroup
+    const int sl = lane % LPR;               // lane within the row
+    const int64_t qh = wg * RWG + rw;
+    const bool ok = qh < QH;                  // (no early exit: the row's lanes shuffle)
+    const int64_t qi = ok ? qh / H : 0;
+    const int h = ok ? (int)(qh % H) : 0;
+    const int c8 = sl * 8;
     const int half = c8 >= D / 2 ? 1 : 0;
-    const int64_t qi = qh / H;
-    const int h = (int)(qh % H);
-    const float mz = sink != nullptr ? sink[h] * LOG2E : -INFINITY;
-    float mx = mz;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, ws_m[(qi * S + s) * H + h]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (mx != -INFINITY) {
-        float L = sink != nullptr ? exp2_fast(mz - mx) : 0.f;
-        for (int s = 0; s < S; ++s)
-            L += exp2_fast(ws_m[(qi * S + s) * H + h] - mx) * ws_l[(qi * S + s) * H + h];
-        const float invL = L > 0.f ? 1.f / L : 0.f;
-        for (int s = 0; s < S; ++s) {
-            const int64_t slot = (qi * S + s) * H + h;
-            const float c = exp2_fast(ws_m[slot] - mx) * ws_l[slot] * invL * ws_x[slot * 2 + half];
-            const u32x4_t v = *(const u32x4_t *)(ws_o + slot * D + c8);
+    const int64_t slot0 = qi * S * H + h;    // slot of split j: slot0 + j * H
+
+    u32x4_t v[SB];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const f32x2_t f = unpack2_f16(v[e]);
-                acc[2 * e] += c * f[0];
-                acc[2 * e + 1] += c * f[1];
+    for (int j = 0; j < SB; ++j)
+        v[j] = ok && j < S ? *(const u32x4_t *)(ws_o + (slot0 + (int64_t)j * H) * D + c8)
+                           : u32x4_t{0, 0, 0, 0};
+    // lane sl holds the scalars of splits sl, sl + LPR, ...
+    float mj[SPL], lj[SPL], x0[SPL], x1[SPL];
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+        const int j = sl + k * LPR;
+        const bool has = ok && j < S;
+        const int64_t slot = slot0 + (int64_t)j * H;
+        mj[k] = has ? ws_m[slot] : -INFINITY;
+        lj[k] = has ? ws_l[slot] : 0.f;
+        x0[k] = has ? ws_x[slot * 2] : 0.f;
+        x1[k] = has ? ws_x[slot * 2 + 1] : 0.f;
+    }
+    const float mz = ok && sink != nullptr ? sink[h] * LOG2E : -INFINITY;
+    float mx = mz;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) mx = fmaxf(mx, mj[k]);
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
+    float L = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < SPL; ++k) L += exp2_fast(mj[k] - mx) * lj[k];
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) L += shfl_xor_f(L, off);
+    if (mx != -INFINITY && sink != nullptr) L += exp2_fast(mz - mx);
+    const float invL = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+        const int j = sl + k * LPR;
+        if (j < S) {
+            const float c = mx != -INFINITY ? exp2_fast(mj[k] - mx) * lj[k] * invL : 0.f;
+            coef[rw][j] = f32x2_t{c * x0[k], c * x1[k]};
+        }
+    }
+    __syncthreads();
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < S; j0 += SB) {
+        if (j0 > 0) {
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+                v[j] = ok && j0 + j < S
+                           ? *(const u32x4_t *)(ws_o + (slot0 + (int64_t)(j0 + j) * H) * D + c8)
+                           : u32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            if (j0 + j < S) {
+                const f32x2_t cc = coef[rw][j0 + j];
+                const float c = half ? cc[1] : cc[0];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const f32x2_t f = unpack2_f16(v[j][e]);
+                    acc[2 * e] += c * f[0];
+                    acc[2 * e + 1] += c * f[1];
+                }
             }
         }
     }
-    const u32x4_t w = {pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]),
-                       pack2_bf16(acc[4], acc[5]), pack2_bf16(acc[6], acc[7])};
-    *(u32x4_t *)(out + qh * D + c8) = w;
+    if (ok) {
+        const u32x4_t w = {pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]),
+                           pack2_bf16(acc[4], acc[5]), pack2_bf16(acc[6], acc[7])};
+        *(u32x4_t *)(out + qh * D + c8) = w;
+    }
 }
 
 __global__ __launch_bounds__(256) void check_idxs_kernel(const int32_t *__restrict__ idxs,
@@ -585,8 +685,16 @@ int device_cu_count() {
     return cache[dev];
 }
 
-// groups of 16 heads per workgroup
-int quads_for(int H) { return H > 32 ? 4 : H > 16 ? 2 : 1; }
+// Workgroup shape for H heads: NHQ wave pairs of HT tiles of 16 heads.
+// 64 heads: four pairs of 16-head waves (two waves per SIMD, so one wave's
+// LDS reads overlap the other's MFMAs); 32 heads: one pair of 32-head waves;
+// up to 16: one pair of 16-head waves.
+struct WgShape {
+    int nhq, ht;
+    int heads() const { return 16 * nhq * ht; }
+};
+WgShape shape_for(int H) { return H > 32 ? WgShape{4, 1} : H > 16 ? WgShape{1, 2} : WgShape{1, 1}; }
+int head_groups(int H) { return (H + shape_for(H).heads() - 1) / shape_for(H).heads(); }
 
 int check_dims(const sa_dims *d) {
     if (d == nullptr) return SA_ERR_NULL;
@@ -620,9 +728,7 @@ WsLayout ws_layout(const sa_dims *d, int S) {
 int plan_splits(const sa_dims *d) {
     const int cus = device_cu_count();
     if (cus < 0) return -SA_ERR_HIP;
-    const int nw = quads_for(d->H);
-    const int64_t hg = (d->H + 16 * nw - 1) / (16 * nw);
-    const int64_t units = queries(d) * hg;
+    const int64_t units = queries(d) * head_groups(d->H);
     if (units <= 0 || units >= cus) return 1;
     int64_t S = (cus + units - 1) / units;
     const int64_t max_by_len = d->K / 64 > 1 ? d->K / 64 : 1;
@@ -631,36 +737,35 @@ int plan_splits(const sa_dims *d) {
     return (int)(S < 1 ? 1 : S);
 }
 
-template <int D, int NHQ>
+template <int D, int NHQ, int HT>
 hipError_t launch_fwd(const FwdParams &p, hipStream_t stream) {
     const int grid = 8 * p.per_xcd;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ>), dim3(grid), dim3(NHQ * 128), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ, HT>), dim3(grid), dim3(NHQ * 128), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_fwd_d(int nw, const FwdParams &p, hipStream_t stream) {
-    switch (nw) {
-        case 1: return launch_fwd<D, 1>(p, stream);
-        case 2: return launch_fwd<D, 2>(p, stream);
-        default: return launch_fwd<D, 4>(p, stream);
-    }
+hipError_t launch_fwd_d(WgShape w, const FwdParams &p, hipStream_t stream) {
+    if (w.ht == 1) return w.nhq == 4 ? launch_fwd<D, 4, 1>(p, stream) : launch_fwd<D, 1, 1>(p, stream);
+    return w.nhq == 2 ? launch_fwd<D, 2, 2>(p, stream) : launch_fwd<D, 1, 2>(p, stream);
 }
 
 hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
                           const void *ws, const WsLayout &L, hipStream_t stream) {
     const int64_t QH = queries(d) * d->H;
-    const int64_t threads = QH * (d->D / 8);
-    const unsigned grid = (unsigned)((threads + 255) / 256);
+    const int rwg = 4 * (64 / (d->D / 8));  // rows per workgroup
+    const int64_t wgs = (QH + rwg - 1) / rwg;
+    const int per_xcd = (int)((wgs + 7) / 8);
+    const unsigned grid = (unsigned)(8 * per_xcd);
     const uint16_t *wo = (const uint16_t *)((const uint8_t *)ws + L.o_off);
     const float *wm = (const float *)((const uint8_t *)ws + L.m_off);
     const float *wl = (const float *)((const uint8_t *)ws + L.l_off);
     const float *wx = (const float *)((const uint8_t *)ws + L.x_off);
     uint16_t *o = (uint16_t *)out;
     switch (d->D) {
-        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S); break;
-        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S); break;
-        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S); break;
+        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd); break;
+        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd); break;
+        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd); break;
     }
     return hipGetLastError();
 }
@@ -716,8 +821,7 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
     p.H = d->H;
     p.K = d->K;
     p.S = S;
-    const int nw = quads_for(d->H);
-    p.HG = (d->H + 16 * nw - 1) / (16 * nw);
+    p.HG = head_groups(d->H);
     const int64_t units = queries(d) * p.HG * S;
     p.units = (int32_t)units;
     p.per_xcd = (int32_t)((units + 7) / 8);
@@ -726,18 +830,16 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
 }
 
 hipError_t run_fwd(const FwdParams &p, int D, int H, hipStream_t stream) {
-    const int nw = quads_for(H);
+    const WgShape w = shape_for(H);
     switch (D) {
-        case 128: return launch_fwd_d<128>(nw, p, stream);
-        case 256: return launch_fwd_d<256>(nw, p, stream);
-        default: return launch_fwd_d<512>(nw, p, stream);
+        case 128: return launch_fwd_d<128>(w, p, stream);
+        case 256: return launch_fwd_d<256>(w, p, stream);
+        default: return launch_fwd_d<512>(w, p, stream);
     }
 }
 
 bool units_fit(const sa_dims *d, int S) {
-    const int nw = quads_for(d->H);
-    const int64_t hg = (d->H + 16 * nw - 1) / (16 * nw);
-    return queries(d) * hg * S <= (int64_t)0x7FFFFFF0;
+    return queries(d) * head_groups(d->H) * S <= (int64_t)0x7FFFFFF0;
 }
 
 }  // namespace

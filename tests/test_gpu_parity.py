@@ -178,6 +178,24 @@ def test_split_counts_agree(ref, S):
     check(ref, w, S, what=f"decode B=4 S={S}")
 
 
+def test_one_workspace_serves_many_calls(ref):
+    # one workspace, calls with different split counts and batch sizes in a
+    # row, each checked against the oracle
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    big = wl.make_decode(B=8)
+    qb, kvb, skb, idxb = to_dev(big)
+    ws = torch.empty(api.workspace_bytes(qb, kvb, idxb, 8), dtype=torch.uint8, device=qb.device)
+    for B, S in ((8, 4), (8, 8), (3, 3), (8, 2), (8, 4)):
+        w = wl.make_decode(B=B)
+        q, kv, sk, idx = to_dev(w)
+        out = api.sparse_attn(q, kv, sk, idx, w.scale, num_splits=S, workspace=ws)
+        torch.cuda.synchronize()
+        got = wl.bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16))
+        exp = ref(w.q, w.kv_host(), w.sink, w.idxs, w.scale)
+        assert_close(got.astype(np.float64), exp, f"shared workspace B={B} S={S}")
+
+
 def test_bitwise_deterministic():
     w = wl.make_decode(B=8)
     for S in (1, 4):
