@@ -37,6 +37,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int KC = 32;                // rows (list entries) per chunk
@@ -178,6 +179,96 @@ __device__ __forceinline__ void wait_vm_ahead(int ahead) {
     if (MAXA >= 2 && ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * STEP) : "memory");
     else if (MAXA >= 1 && ahead >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(STEP) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// a7 / a8: epilogue shared by the attention kernels.  Lane (li, g) of wave
+// (hq, dh) holds O^T[dh*D/2 + 16u + 4g + i, h] of head tile t, with the
+// softmax state (m, lsum) of head h = hg*HWG + hq*HW + 16t + li.  Every output
+// (final, or a split's partial) is normalised by its own denominator, then
+// staged through LDS (HWG rows of 2D bytes at `stage_out`, which the caller
+// has freed with a barrier) so that each wave instruction stores whole rows:
+// the final output as bf16, a split's partial as fp16 scaled by a power of
+// two.  In LDS, 16-byte chunk c of head row hl sits at position c ^ swz(hl),
+// which keeps the 16 rows written by one store instruction on distinct banks.
+template <int D, int NHQ, int HT>
+__device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t (&o)[HT][D / 32],
+                                              const float (&m)[HT], const float (&lsum)[HT],
+                                              int qi, int s, int hg, LDS_AS uint8_t *stage_out) {
+    constexpr int NT = NHQ * 128;
+    constexpr int HW = 16 * HT;
+    constexpr int HWG = NHQ * HW;
+    constexpr int DTH = D / 32;
+    constexpr int C16 = D / 8;  // 16-byte chunks per 16-bit row
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int hq = wid >> 1, dh = wid & 1, g = lane >> 4, li = lane & 15;
+    const int hbase = hg * HWG;
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+        const int h = hbase + hq * HW + 16 * t + li;
+        const bool h_ok = h < p.H;
+        const int hl = hq * HW + 16 * t + li;  // head row within the workgroup
+        float ltot = lsum[t] + shfl_xor_f(lsum[t], 16);
+        ltot += shfl_xor_f(ltot, 32);
+        float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
+        if (p.S == 1) {
+            if (p.sink != nullptr && h_ok) {
+                // the sink joins the softmax: M = max(m, sink), L = l 2^(m-M) + 2^(sink-M)
+                const float zs = p.sink[h] * LOG2E;
+                const float M = fmaxf(m[t], zs);
+                const float alpha = m[t] == -INFINITY ? 0.f : exp2_fast(m[t] - M);
+                inv = alpha / (ltot * alpha + exp2_fast(zs - M));
+            }
+#pragma unroll
+            for (int u = 0; u < DTH; ++u) {
+                const int col = dh * (D / 2) + 16 * u + 4 * g;  // first of 4 columns
+                const int pos = (col >> 3) ^ swz<C16>(hl);
+                const u32x2_t w = {pack2_bf16(o[t][u][0] * inv, o[t][u][1] * inv),
+                                   pack2_bf16(o[t][u][2] * inv, o[t][u][3] * inv)};
+                *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
+            }
+        } else {
+            // A split's partial: fp16 rows (11 significant bits) scaled by a
+            // power of two per (head, half row) so that |value| < 2^15 never
+            // overflows.
+            float amax = 0.f;
+#pragma unroll
+            for (int u = 0; u < DTH; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[t][u][i] * inv));
+            amax = fmaxf(amax, shfl_xor_f(amax, 16));
+            amax = fmaxf(amax, shfl_xor_f(amax, 32));
+            int ex = 0;
+            if (amax < INFINITY) (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1)
+            const int e = ex > 15 ? ex - 15 : 0;
+            const float down = ldexpf(inv, -e);
+#pragma unroll
+            for (int u = 0; u < DTH; ++u) {
+                const int col = dh * (D / 2) + 16 * u + 4 * g;
+                const int pos = (col >> 3) ^ swz<C16>(hl);
+                const u32x2_t w = {pack2_f16(o[t][u][0] * down, o[t][u][1] * down),
+                                   pack2_f16(o[t][u][2] * down, o[t][u][3] * down)};
+                *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
+            }
+            if (g == 0 && h_ok) {
+                const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
+                p.ws_x[slot * 2 + dh] = ldexpf(1.f, e);
+                if (dh == 0) {
+                    p.ws_m[slot] = m[t];
+                    p.ws_l[slot] = ltot;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    uint16_t *dst = p.S == 1 ? p.out + (int64_t)qi * p.H * D
+                             : p.ws_o + ((int64_t)qi * p.S + s) * p.H * D;
+    for (int i = tid; i < HWG * C16; i += NT) {
+        const int r = i / C16, pos = i % C16;
+        const u32x4_t v = *(const LDS_AS u32x4_t *)(stage_out + r * (D * 2) + pos * 16);
+        if (hbase + r < p.H)
+            *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v;
+    }
 }
 
 // Work split: a workgroup holds NHQ groups of 16*HT heads; each group is
@@ -461,85 +552,252 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         }
     }
 
-    // a7 / a8: epilogue.  Lane (li, g) holds O^T[dh*D/2 + 16u + 4g + i, h] of
-    // head tile t.  Every output (final, or a split's partial) is normalised
-    // by its own denominator, then staged through the (now idle) LDS ring so
-    // that each wave instruction stores 1 KB of contiguous rows: the final
-    // output as bf16, a split's partial as fp16 scaled by a power of two.  In
-    // LDS, 16-byte chunk c of head row hl sits at position c ^ swz(hl), which
-    // keeps the 16 rows written by one store instruction on distinct banks.
+    // a7 / a8: epilogue
+    static_assert(HWG * D * 2 <= NBUF * KC * RS, "output staging fits in the ring");
     __syncthreads();  // every wave is done with the ring; reuse it for staging
-    LDS_AS uint8_t *stage_out = (LDS_AS uint8_t *)&tile[0][0];
-    const int hbase = hg * HWG;
-    constexpr int C16 = D / 8;  // 16-byte chunks per 16-bit row
-    static_assert(HWG * D * 2 <= NBUF * KC * RS, "staging fits in the ring");
+    store_outputs<D, NHQ, HT>(p, o, m, lsum, qi, s, hg, (LDS_AS uint8_t *)&tile[0][0]);
+}
+
+// Many-query variant, for launches with at least two workgroups per compute
+// unit (prefill), where MFMA throughput rather than gather depth decides.
+// Same steps and results as attn_fwd_kernel; the work is split differently:
+//   * a pair of waves serves 32 heads.  For QK^T and the softmax each wave
+//     takes one tile of 16 heads over the whole of d (no partial scores to
+//     add up); the pair then swaps its bf16 weights (and rescale factors)
+//     through LDS, and for PV each wave takes one half of d for both tiles,
+//     so every V operand read from LDS feeds two MFMAs;
+//   * a 2-chunk ring of 32 padded rows, the weight exchange and the list
+//     (compacted in place, sized by K in dynamic LDS) take about 75 KB of
+//     LDS, so two workgroups share a compute unit and one's softmax,
+//     barriers, prologue and epilogue overlap the other's MFMAs.
+// q is staged in the ring in the prologue (padded rows, one head per row).
+template <int D, int NHQ>
+__global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) {
+    constexpr int HT = 2;                  // head tiles per pair
+    constexpr int NW = 2 * NHQ;            // waves per workgroup
+    constexpr int NT = NW * 64;
+    constexpr int HP = 16 * HT;            // heads per pair
+    constexpr int ROWB = D * 2;
+    constexpr int RS = ROWB + 32;          // padded ring row (see attn_fwd_kernel)
+    constexpr int CPR = D / 8;
+    constexpr int NB = 2;                  // ring chunks
+    constexpr int IPW = KC / NW;           // DMA instructions (one row each) per wave per chunk
+    constexpr int DS = D / 32;             // MFMA k-steps over d
+    constexpr int DTH = D / 32;            // 16-wide output tiles in one half of d
+    static_assert(KC % NW == 0 && IPW <= 63, "ring shape");
+    static_assert(NW * 16 * RS <= NB * KC * RS, "q of the workgroup fits the ring");
+    static_assert(NHQ * HP * D * 2 <= NB * KC * RS, "output staging fits in the ring");
+
+    __shared__ __attribute__((aligned(16))) uint8_t tile[NB][KC * RS];
+    __shared__ __attribute__((aligned(16))) u32x4_t xp[NW][64];  // bf16 weights of the tile
+    __shared__ float xa[NW][64];                                  // rescale factor / final state
+    __shared__ int32_t cnt[8 * NW];
+    extern __shared__ int32_t list[];  // K entries: raw, then compacted in place
+
+    const int bid = blockIdx.x;
+    const int unit = (bid & 7) * p.per_xcd + (bid >> 3);
+    if (unit >= p.units) return;
+    const int s = unit % p.S;
+    const int hg = (unit / p.S) % p.HG;
+    const int qi = unit / (p.S * p.HG);
+    const int b = qi / p.T;
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int hq = wid >> 1;      // pair
+    const int w = wid & 1;        // own head tile (QK^T, softmax) and half of d (PV)
+    const int g = lane >> 4, li = lane & 15;
+    const int hown = hg * (NHQ * HP) + hq * HP + 16 * w + li;  // head of this lane's scores
+    const uint16_t *kvb = p.kv + (int64_t)b * p.N * D;
+
+    // Prologue: the raw list into `list`, this wave's 16 q rows (whole d,
+    // head hh at qstage + hh*RS) into the ring, both by LDS-DMA.
+    {
+        const int32_t *lst = p.idxs + (int64_t)qi * p.K;
+        const int NI = (p.K + 63) / 64;
+        for (int i = wid; i < NI; i += NW) {
+            const int k = i * 64 + lane;
+            if (k < p.K) lds_dma4(lst + k, (LDS_AS int32_t *)list + i * 64);
+        }
+    }
+    LDS_AS uint8_t *qstage = (LDS_AS uint8_t *)&tile[0][0] + wid * (16 * RS);
+    {
+        const int h0 = hown - li;
 #pragma unroll
-    for (int t = 0; t < HT; ++t) {
-        const int h = hw0 + 16 * t + li;
-        const bool h_ok = h < p.H;
-        const int hl = hq * HW + 16 * t + li;  // head row within the workgroup
-        float ltot = lsum[t] + shfl_xor_f(lsum[t], 16);
-        ltot += shfl_xor_f(ltot, 32);
-        float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
-        if (p.S == 1) {
-            if (p.sink != nullptr && h_ok) {
-                // the sink joins the softmax: M = max(m, sink), L = l 2^(m-M) + 2^(sink-M)
-                const float zs = p.sink[h] * LOG2E;
-                const float M = fmaxf(m[t], zs);
-                const float alpha = m[t] == -INFINITY ? 0.f : exp2_fast(m[t] - M);
-                inv = alpha / (ltot * alpha + exp2_fast(zs - M));
+        for (int hh = 0; hh < 16; ++hh) {
+            const int hsrc = h0 + hh < p.H ? h0 + hh : 0;  // zeroed below
+            if (CPR == 64 || lane < CPR)
+                lds_dma16(p.q + ((int64_t)qi * p.H + hsrc) * D + lane * 8, qstage + hh * RS);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // a1: decode and compact the list (in place), then take this split's slice.
+    const int n = compact_list<NT>((const LDS_AS int32_t *)list, p.K, p.N, list, cnt);
+    const int lo = (int)(((int64_t)n * s) / p.S);
+    const int hi = (int)(((int64_t)n * (s + 1)) / p.S);
+    const int nchunks = (hi - lo + KC - 1) / KC;
+
+    // a3: qf[k] = q[hown, 32k + 8g .. +7], the B operands over the whole of d
+    bf16x8_t qf[DS];
+    {
+        const bool ok = hown < p.H;
+#pragma unroll
+        for (int k = 0; k < DS; ++k) {
+            u32x4_t v = *(const LDS_AS u32x4_t *)(qstage + li * RS + (4 * k + g) * 16);
+            if (!ok) v = u32x4_t{0, 0, 0, 0};
+            qf[k] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+    __syncthreads();  // q is in registers: the ring is free
+
+    // a2: chunk c (KC rows) into ring slot c % NB, one row per DMA instruction;
+    // tail slots repeat the chunk's first row (masked below).
+    auto stage = [&](int c) {
+        const int e0 = lo + c * KC;
+        uint8_t *buf = &tile[c % NB][0];
+        int row[IPW];
+#pragma unroll
+        for (int k = 0; k < IPW; ++k) {
+            const int e = e0 + k * NW + wid;
+            row[k] = list[e < hi ? e : e0];
+        }
+#pragma unroll
+        for (int k = 0; k < IPW; ++k) {
+            const int r = k * NW + wid;
+            if (CPR == 64 || lane < CPR)
+                lds_dma16(kvb + (int64_t)row[k] * D + lane * 8,
+                          (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS));
+        }
+    };
+    if (nchunks > 0) stage(0);
+    if (nchunks > 1) stage(1);
+
+    float m = -INFINITY, lsum = 0.f;  // softmax state of head hown (log2 units)
+    f32x4_t o[HT][DTH];               // O^T of both tiles over this wave's half of d
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+        for (int u = 0; u < DTH; ++u) o[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = 0; c < nchunks; ++c) {
+        // chunk c has landed once at most the chunk after it is pending
+        wait_vm_ahead<IPW, 1>(c == 0 && nchunks > 1 ? 1 : 0);
+        __syncthreads();
+        if (c >= 1 && c + 1 < nchunks) stage(c + 1);
+
+        const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NB][0];
+        const int cnt_c = min(KC, hi - (lo + c * KC));
+
+        // a4: S^T[j, hown] over the whole of d, rows j = 16 jt + 4 g + i.
+        // Software-pipelined by hand: operand load i + QKP is issued right
+        // after MFMA i, and the scheduling barriers keep that order (left
+        // alone, the scheduler issues each load next to its MFMA and the LDS
+        // latency is exposed on every one).
+        f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        {
+            constexpr int QKP = 4, NQK = 2 * DS;
+            auto kload = [&](int i) {  // operand i: k-step i/2, row tile i%2
+                return __builtin_bit_cast(bf16x8_t, *(const LDS_AS u32x4_t *)(
+                    T + ((i & 1) * 16 + li) * RS + (4 * (i >> 1) + g) * 16));
+            };
+            bf16x8_t ka[QKP];
+#pragma unroll
+            for (int i = 0; i < QKP; ++i) ka[i] = kload(i);
+#pragma unroll
+            for (int i = 0; i < NQK; ++i) {
+                sacc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i % QKP], qf[i >> 1],
+                                                                      sacc[i & 1], 0, 0, 0);
+                if (i + QKP < NQK) ka[i % QKP] = kload(i + QKP);
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
+
+        // a5: online softmax of the own tile (lazy max, as in attn_fwd_kernel)
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = 16 * (e >> 2) + 4 * g + (e & 3);
+            sv[e] = cnt_c == KC || j < cnt_c ? sacc[e >> 2][e & 3] * p.qk_scale_log2 : -INFINITY;
+        }
+        const float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                 fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        float alpha = 1.f;
+        if (__ballot(lmax > m + MAX_SLACK)) {
+            float cmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
+            cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+            const float mnew = cmax > m + MAX_SLACK ? cmax : m;
+            alpha = exp2_fast(m - mnew);
+            lsum *= alpha;
+            m = mnew;
+        }
+        const u32x4_t pw = {pack2_bf16(exp2_fast(sv[0] - m), exp2_fast(sv[1] - m)),
+                            pack2_bf16(exp2_fast(sv[2] - m), exp2_fast(sv[3] - m)),
+                            pack2_bf16(exp2_fast(sv[4] - m), exp2_fast(sv[5] - m)),
+                            pack2_bf16(exp2_fast(sv[6] - m), exp2_fast(sv[7] - m))};
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            psum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
+        lsum += psum;
+
+        // the pair swaps weights and rescale factors
+        xp[wid][lane] = pw;
+        if (g == 0) xa[wid][li] = alpha;
+        __syncthreads();
+        const u32x4_t pp = xp[wid ^ 1][lane];
+        const float alpha_p = xa[wid ^ 1][li];
+        const bf16x8_t p0 = __builtin_bit_cast(bf16x8_t, w == 0 ? pw : pp);
+        const bf16x8_t p1 = __builtin_bit_cast(bf16x8_t, w == 0 ? pp : pw);
+        const float a0 = w == 0 ? alpha : alpha_p, a1 = w == 0 ? alpha_p : alpha;
+        if (__ballot(a0 != 1.f)) {
+#pragma unroll
+            for (int u = 0; u < DTH; ++u) o[0][u] *= a0;
+        }
+        if (__ballot(a1 != 1.f)) {
+#pragma unroll
+            for (int u = 0; u < DTH; ++u) o[1][u] *= a1;
+        }
+
+        // a6: O^T[d, h] += V^T[d, j] P^T[j, h] over this wave's half of d; the
+        // transpose loads hand lane (li, g) column 16tt + li of rows 4g..4g+3
+        // and 16+4g..16+4g+3, the k-slots of its weights
+        // (pipelined by hand like QK^T: transpose pair u + PVP is loaded right
+        // after the two MFMAs of pair u)
+        {
+            constexpr int PVP = 3;
+            const LDS_AS uint8_t *R0 = T + (4 * g + (li >> 2)) * RS + (li & 3) * 8;
+            const LDS_AS uint8_t *R1 = R0 + 16 * RS;
+            auto vload = [&](int u) {
+                const int off = (w * DTH + u) * 32;
+                const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R0 + off));
+                const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R1 + off));
+                return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            bf16x8_t va[PVP];
+#pragma unroll
+            for (int u = 0; u < PVP; ++u) va[u] = vload(u);
 #pragma unroll
             for (int u = 0; u < DTH; ++u) {
-                const int col = dh * (D / 2) + 16 * u + 4 * g;  // first of 4 columns
-                const int pos = (col >> 3) ^ swz<C16>(hl);
-                const u32x2_t w = {pack2_bf16(o[t][u][0] * inv, o[t][u][1] * inv),
-                                   pack2_bf16(o[t][u][2] * inv, o[t][u][3] * inv)};
-                *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
-            }
-        } else {
-            // A split's partial: fp16 rows (11 significant bits) scaled by a
-            // power of two per (head, half row) so that |value| < 2^15 never
-            // overflows.
-            float amax = 0.f;
-#pragma unroll
-            for (int u = 0; u < DTH; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[t][u][i] * inv));
-            amax = fmaxf(amax, shfl_xor_f(amax, 16));
-            amax = fmaxf(amax, shfl_xor_f(amax, 32));
-            int ex = 0;
-            if (amax < INFINITY) (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1)
-            const int e = ex > 15 ? ex - 15 : 0;
-            const float down = ldexpf(inv, -e);
-#pragma unroll
-            for (int u = 0; u < DTH; ++u) {
-                const int col = dh * (D / 2) + 16 * u + 4 * g;
-                const int pos = (col >> 3) ^ swz<C16>(hl);
-                const u32x2_t w = {pack2_f16(o[t][u][0] * down, o[t][u][1] * down),
-                                   pack2_f16(o[t][u][2] * down, o[t][u][3] * down)};
-                *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
-            }
-            if (g == 0 && h_ok) {
-                const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
-                p.ws_x[slot * 2 + dh] = ldexpf(1.f, e);
-                if (dh == 0) {
-                    p.ws_m[slot] = m[t];
-                    p.ws_l[slot] = ltot;
-                }
+                o[0][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u % PVP], p0, o[0][u], 0, 0, 0);
+                o[1][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u % PVP], p1, o[1][u], 0, 0, 0);
+                if (u + PVP < DTH) va[u % PVP] = vload(u + PVP);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
+
+    // a7 / a8: epilogue.  The pair swaps its final softmax state so that each
+    // wave can normalise both tiles of its half of d.
+    __syncthreads();  // every wave is done with the ring and the exchange buffers
+    xa[wid][lane] = lsum;
+    if (g == 0) *(LDS_AS float *)&xp[wid][li] = m;
     __syncthreads();
-    uint16_t *dst = p.S == 1 ? p.out + (int64_t)qi * p.H * D
-                             : p.ws_o + ((int64_t)qi * p.S + s) * p.H * D;
-    for (int i = tid; i < HWG * C16; i += NT) {
-        const int r = i / C16, pos = i % C16;
-        const u32x4_t v = *(const LDS_AS u32x4_t *)(stage_out + r * (D * 2) + pos * 16);
-        if (hbase + r < p.H)
-            *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v;
-    }
+    const float lsum_p = xa[wid ^ 1][lane];
+    const float m_p = *(const LDS_AS float *)&xp[wid ^ 1][li];
+    const float mt[HT] = {w == 0 ? m : m_p, w == 0 ? m_p : m};
+    const float lt[HT] = {w == 0 ? lsum : lsum_p, w == 0 ? lsum_p : lsum};
+    store_outputs<D, NHQ, HT>(p, o, mt, lt, qi, s, hg, (LDS_AS uint8_t *)&tile[0][0]);
 }
 
 // a9: log-sum-exp merge of the splits.  Split s holds p_s (its output
@@ -829,7 +1087,31 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
     return p;
 }
 
+template <int D, int NHQ>
+hipError_t launch_mq(const FwdParams &p, hipStream_t stream) {
+    const int grid = 8 * p.per_xcd;
+    const size_t list_bytes = ((size_t)(p.K > 0 ? p.K : 1) * 4 + 15) / 16 * 16;
+    hipLaunchKernelGGL((attn_fwd_mq_kernel<D, NHQ>), dim3(grid), dim3(NHQ * 128), list_bytes,
+                       stream, p);
+    return hipGetLastError();
+}
+
+// The many-query kernel pays off once two of its workgroups can share every
+// compute unit; below that the deep-ring kernel keeps more rows in flight.
+bool use_mq(const FwdParams &p, int H) {
+    const int cus = device_cu_count();
+    return H > 16 && cus > 0 && (int64_t)p.units >= 2 * (int64_t)cus;
+}
+
 hipError_t run_fwd(const FwdParams &p, int D, int H, hipStream_t stream) {
+    if (use_mq(p, H)) {
+        const bool two = H > 32;
+        switch (D) {
+            case 128: return two ? launch_mq<128, 2>(p, stream) : launch_mq<128, 1>(p, stream);
+            case 256: return two ? launch_mq<256, 2>(p, stream) : launch_mq<256, 1>(p, stream);
+            default: return two ? launch_mq<512, 2>(p, stream) : launch_mq<512, 1>(p, stream);
+        }
+    }
     const WgShape w = shape_for(H);
     switch (D) {
         case 128: return launch_fwd_d<128>(w, p, stream);

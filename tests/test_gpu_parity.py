@@ -215,6 +215,40 @@ def test_check_idxs_counts_out_of_range():
     assert check_idxs(torch.from_numpy(bad).cuda(), w.N) == 3
 
 
+# ------------------------------------------------- many-query path (prefill)
+# Launches with at least two workgroups per compute unit run the many-query
+# kernel (two workgroups share a compute unit); these cases reach it at sizes
+# the oracle finishes quickly.
+
+def many_query_T(B=2):
+    torch = torch_mod()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return (2 * cus + 8 + B - 1) // B
+
+
+@pytest.mark.parametrize("H,D", [(64, 512), (48, 512), (32, 256), (20, 128)])
+def test_many_query_path(ref, H, D):
+    # K=75 with ~30% unused: one full 32-row chunk, a ragged one, varying counts
+    w = wl.make_random(200 + H + D, 2, many_query_T(), H, D, 160, 75, p_unused=0.3)
+    check(ref, w, 0, what=f"many-query H={H} D={D}")
+
+
+def test_many_query_splits_stress_and_long_lists(ref):
+    T = many_query_T()
+    w = wl.make_random(210, 2, T, 64, 512, 120, 40, p_unused=0.2)
+    check(ref, w, 2, what="many-query S=2")
+    q8 = wl.to_bf16_bits(wl.bf16_bits_to_f32(w.q) * 8.0)
+    check(ref, w, 0, q_bits=q8, what="many-query 8x query")
+    check(ref, w, 0, sink=np.full(64, 30.0), what="many-query sink=30")
+    got = run_gpu(w, 0, np.full(w.idxs.shape, -1, np.int32))
+    assert np.all(got == 0)
+    got0 = run_gpu(w, 0, np.zeros((2, T, 0), np.int32))
+    assert np.all(got0 == 0)
+    # the longest supported list (2048 entries, compacted in place), mostly unused
+    wl2 = wl.make_random(211, 1, 2 * T, 64, 512, 2100, 2048, p_unused=0.97)
+    check(ref, wl2, 0, what="many-query K=2048")
+
+
 # --------------------------------------------------------- full-size workloads
 # Same launch configuration as bench.py: num_splits=0 (planned by the library).
 
