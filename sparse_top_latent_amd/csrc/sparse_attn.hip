@@ -63,7 +63,7 @@ struct FwdParams {
     float *ws_x;       // [Q, S, H, 2] power-of-two scale of each half row of ws_o
     int64_t N;
     int32_t T, H, K;
-    int32_t S, HG, units, per_xcd;
+    int32_t S, HG, units, per_xcd, bs;  // see unit_of
     float qk_scale_log2;  // scale * log2(e)
 };
 
@@ -80,6 +80,19 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup -> unit (one (query, head group, split) each), or -1 for a spare
+// workgroup.  Workgroups go to the eight XCDs round-robin by blockIdx; XCD x
+// runs blocks x, x+8, x+16, ... of bs consecutive units, so the splits and
+// head groups of a query (bs is a multiple of their count) and neighbouring
+// queries share an XCD's L2, while every XCD gets a share of every part of
+// the batch.  Units run in reverse order: in causal prefill the late queries
+// have the longest lists, and starting them first shortens the tail.
+__device__ __forceinline__ int unit_of(int bid, int units, int bs) {
+    const int x = bid & 7, j = bid >> 3;
+    const int u = ((j / bs) * 8 + x) * bs + (j % bs);
+    return u < units ? units - 1 - u : -1;
+}
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, 64);
@@ -158,6 +171,17 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, const LDS_AS void *l
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(gptr), "s"(m0)
+                 : "memory", "m0");
+}
+
+// Same with a wave-uniform row base in SGPRs and a per-lane byte offset
+// (saddr form: no 64-bit per-lane address arithmetic).
+__device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff,
+                                            const LDS_AS void *lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0)
                  : "memory", "m0");
 }
 
@@ -309,11 +333,9 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     __shared__ int32_t list[LIST_CAP];
     __shared__ int32_t cnt[8 * NW];
 
-    // XCD-aware unit order: consecutive units (the splits and head groups of
-    // one query, or neighbouring queries) run on the same XCD and share its L2.
     const int bid = blockIdx.x;
-    const int unit = (bid & 7) * p.per_xcd + (bid >> 3);
-    if (unit >= p.units) return;
+    const int unit = unit_of(bid, p.units, p.bs);
+    if (unit < 0) return;
     const int s = unit % p.S;
     const int hg = (unit / p.S) % p.HG;
     const int qi = unit / (p.S * p.HG);
@@ -595,8 +617,8 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     extern __shared__ int32_t list[];  // K entries: raw, then compacted in place
 
     const int bid = blockIdx.x;
-    const int unit = (bid & 7) * p.per_xcd + (bid >> 3);
-    if (unit >= p.units) return;
+    const int unit = unit_of(bid, p.units, p.bs);
+    if (unit < 0) return;
     const int s = unit % p.S;
     const int hg = (unit / p.S) % p.HG;
     const int qi = unit / (p.S * p.HG);
@@ -651,27 +673,29 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     }
     __syncthreads();  // q is in registers: the ring is free
 
-    // a2: chunk c (KC rows) into ring slot c % NB, one row per DMA instruction;
-    // tail slots repeat the chunk's first row (masked below).
-    auto stage = [&](int c) {
+    // a2: chunk c (KC rows) into ring slot c % NB, one row per DMA
+    // instruction (row r = k*NW + wid for the wave's k-th); tail slots repeat
+    // the chunk's first row (masked below).  rows_of reads the chunk's row
+    // numbers one chunk ahead (lane k holds the k-th), so a stage only moves
+    // them to SGPRs and issues the DMAs.
+    auto rows_of = [&](int c) {
         const int e0 = lo + c * KC;
-        uint8_t *buf = &tile[c % NB][0];
-        int row[IPW];
+        const int e = e0 + (lane % IPW) * NW + wid;
+        return list[e < hi ? e : e0];
+    };
+    auto stage = [&](int c, int rows) {
+        LDS_AS uint8_t *buf = (LDS_AS uint8_t *)&tile[c % NB][0];
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
-            const int e = e0 + k * NW + wid;
-            row[k] = list[e < hi ? e : e0];
-        }
-#pragma unroll
-        for (int k = 0; k < IPW; ++k) {
-            const int r = k * NW + wid;
-            if (CPR == 64 || lane < CPR)
-                lds_dma16(kvb + (int64_t)row[k] * D + lane * 8,
-                          (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS));
+            const int row = __builtin_amdgcn_readlane(rows, k);
+            const uint16_t *src = kvb + (int64_t)row * D;
+            if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, buf + (k * NW + wid) * RS);
         }
     };
-    if (nchunks > 0) stage(0);
-    if (nchunks > 1) stage(1);
+    int next_rows = 0;
+    if (nchunks > 0) stage(0, rows_of(0));
+    if (nchunks > 1) stage(1, rows_of(1));
+    if (nchunks > 2) next_rows = rows_of(2);
 
     float m = -INFINITY, lsum = 0.f;  // softmax state of head hown (log2 units)
     f32x4_t o[HT][DTH];               // O^T of both tiles over this wave's half of d
@@ -684,7 +708,10 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         // chunk c has landed once at most the chunk after it is pending
         wait_vm_ahead<IPW, 1>(c == 0 && nchunks > 1 ? 1 : 0);
         __syncthreads();
-        if (c >= 1 && c + 1 < nchunks) stage(c + 1);
+        if (c >= 1 && c + 1 < nchunks) {
+            stage(c + 1, next_rows);
+            if (c + 2 < nchunks) next_rows = rows_of(c + 2);
+        }
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NB][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
@@ -829,7 +856,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     __shared__ f32x2_t coef[RWG][MAX_SPLITS];
 
     const int bid = blockIdx.x;
-    const int64_t wg = (int64_t)(bid & 7) * per_xcd + (bid >> 3);
+    // reversed blocks per XCD, like the attention kernels' unit order (the
+    // partials of a query were written on the XCD that merges them)
+    const int64_t wg = (int64_t)8 * per_xcd - 1 - ((int64_t)(bid & 7) * per_xcd + (bid >> 3));
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int rw = wid * RPW + lane / LPR;   // row within the workgroup
     const int sl = lane % LPR;               // lane within the row
@@ -1082,7 +1111,12 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
     p.HG = head_groups(d->H);
     const int64_t units = queries(d) * p.HG * S;
     p.units = (int32_t)units;
-    p.per_xcd = (int32_t)((units + 7) / 8);
+    // blocks of up to 64 queries' units per XCD turn (see unit_of)
+    const int64_t per_q = (int64_t)p.HG * S;
+    const int64_t even = (units + 7) / 8;
+    const int64_t bs = even < 64 * per_q ? even : 64 * per_q;
+    p.bs = (int32_t)bs;
+    p.per_xcd = (int32_t)(((even + bs - 1) / bs) * bs);
     p.qk_scale_log2 = scale * LOG2E;
     return p;
 }
@@ -1120,8 +1154,11 @@ hipError_t run_fwd(const FwdParams &p, int D, int H, hipStream_t stream) {
     }
 }
 
+// unit and workgroup numbers (including the spare workgroups of the last
+// XCD turn, at most 8 blocks of 64 queries' units) stay below 2^31
 bool units_fit(const sa_dims *d, int S) {
-    return queries(d) * head_groups(d->H) * S <= (int64_t)0x7FFFFFF0;
+    const int64_t per_q = (int64_t)head_groups(d->H) * S;
+    return queries(d) * per_q + 512 * per_q <= (int64_t)0x7FFFFFF0;
 }
 
 }  // namespace
