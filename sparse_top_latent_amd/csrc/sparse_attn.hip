@@ -683,14 +683,15 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         const int e = e0 + (lane % IPW) * NW + wid;
         return list[e < hi ? e : e0];
     };
-    auto stage = [&](int c, int rows) {
+    auto stage_one = [&](int c, int rows, int k) {  // this wave's k-th row of chunk c
         LDS_AS uint8_t *buf = (LDS_AS uint8_t *)&tile[c % NB][0];
+        const int row = __builtin_amdgcn_readlane(rows, k);
+        const uint16_t *src = kvb + (int64_t)row * D;
+        if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, buf + (k * NW + wid) * RS);
+    };
+    auto stage = [&](int c, int rows) {
 #pragma unroll
-        for (int k = 0; k < IPW; ++k) {
-            const int row = __builtin_amdgcn_readlane(rows, k);
-            const uint16_t *src = kvb + (int64_t)row * D;
-            if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, buf + (k * NW + wid) * RS);
-        }
+        for (int k = 0; k < IPW; ++k) stage_one(c, rows, k);
     };
     int next_rows = 0;
     if (nchunks > 0) stage(0, rows_of(0));
@@ -708,10 +709,10 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         // chunk c has landed once at most the chunk after it is pending
         wait_vm_ahead<IPW, 1>(c == 0 && nchunks > 1 ? 1 : 0);
         __syncthreads();
-        if (c >= 1 && c + 1 < nchunks) {
-            stage(c + 1, next_rows);
-            if (c + 2 < nchunks) next_rows = rows_of(c + 2);
-        }
+        // chunk c + 1 goes into the slot chunk c - 1 left; its DMAs are spread
+        // through the QK^T MFMAs below, so that a wave never waits for a burst
+        // of them to be accepted
+        const bool do_stage = c >= 1 && c + 1 < nchunks;
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NB][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
@@ -736,9 +737,15 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
                 sacc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i % QKP], qf[i >> 1],
                                                                       sacc[i & 1], 0, 0, 0);
                 if (i + QKP < NQK) ka[i % QKP] = kload(i + QKP);
+                if (do_stage) {  // DMAs k in [i*IPW/NQK, (i+1)*IPW/NQK): spread evenly
+#pragma unroll
+                    for (int k = i * IPW / NQK; k < (i + 1) * IPW / NQK; ++k)
+                        stage_one(c + 1, next_rows, k);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if (do_stage && c + 2 < nchunks) next_rows = rows_of(c + 2);
 
         // a5: online softmax of the own tile (lazy max, as in attn_fwd_kernel)
         float sv[8];
