@@ -116,48 +116,48 @@ __device__ __forceinline__ f32x2_t unpack2_f16(uint32_t w) {
     return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
 }
 
-// a1: index decode + compaction of a list already staged in LDS.  The list
-// is read in groups of EG rounds of NT entries: every thread reads its (up
-// to) EG entries of a group, a ballot per round gives each valid entry its
-// slot, and one barrier publishes the per-wave counts.  Entries keep their
-// order.  Returns the number of valid entries (0 <= idx < N).
+// a1: index decode + compaction of a list already staged in LDS.  Wave w
+// takes a contiguous segment of the list (a multiple of 64 entries); a ballot
+// per 64 entries ranks its valid entries, one barrier publishes the per-wave
+// counts, and each wave writes its entries after those of the waves before
+// it, so the order is kept.  All reads of `lst` happen before the first
+// barrier and all writes after it, so `list` may be `lst` (compaction in
+// place).  cnt holds NT/64 ints.  Returns the number of valid entries
+// (0 <= idx < N); `list` is complete for every wave on return.
 template <int NT>
 __device__ int compact_list(const LDS_AS int32_t *lst, int K, int64_t N, int32_t *list,
-                            int32_t *cnt /* [EG][NT/64] */) {
+                            int32_t *cnt) {
     constexpr int NWV = NT / 64;
-    constexpr int EG = 8;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    int base = 0;
-    for (int k0 = 0; k0 < K; k0 += EG * NT) {
-        int v[EG];
-        uint64_t mask[EG];
+    constexpr int MAXR = (LIST_CAP + NT - 1) / NT;  // rounds of 64 per wave, at most
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int seg = ((K + NWV - 1) / NWV + 63) / 64 * 64;
+    const int k0 = wid * seg;
+    int v[MAXR];
+    uint64_t mask[MAXR];
+    int total = 0;
 #pragma unroll
-        for (int r = 0; r < EG; ++r) {
-            const int k = k0 + r * NT + tid;
-            v[r] = k < K ? lst[k] : -1;
-        }
-#pragma unroll
-        for (int r = 0; r < EG; ++r) {
-            mask[r] = __ballot(v[r] >= 0 && (int64_t)v[r] < N);
-            if (lane == 0) cnt[r * NWV + wid] = __popcll(mask[r]);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < EG; ++r) {
-            int before_waves = 0, round = 0;
-#pragma unroll
-            for (int w = 0; w < NWV; ++w) {
-                const int c = cnt[r * NWV + w];
-                before_waves += w < wid ? c : 0;
-                round += c;
-            }
-            if ((mask[r] >> lane) & 1ull)
-                list[base + before_waves + __popcll(mask[r] & ((1ull << lane) - 1ull))] = v[r];
-            base += round;
-        }
-        __syncthreads();
+    for (int r = 0; r < MAXR; ++r) {
+        const int k = k0 + r * 64 + lane;
+        v[r] = r * 64 < seg && k < K ? lst[k] : -1;
+        mask[r] = __ballot(v[r] >= 0 && (int64_t)v[r] < N);
+        total += __popcll(mask[r]);
     }
-    return base;
+    if (lane == 0) cnt[wid] = total;
+    __syncthreads();
+    int base = 0, n = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+        const int c = cnt[w];
+        base += w < wid ? c : 0;
+        n += c;
+    }
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+        if ((mask[r] >> lane) & 1ull) list[base + __popcll(mask[r] & ((1ull << lane) - 1ull))] = v[r];
+        base += __popcll(mask[r]);
+    }
+    __syncthreads();
+    return n;
 }
 
 // One LDS-DMA wave instruction: every lane fetches 16 bytes from its own
@@ -285,13 +285,23 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
         }
     }
     __syncthreads();
+    // every LDS read first, then every store (one LDS round trip in all)
     uint16_t *dst = p.S == 1 ? p.out + (int64_t)qi * p.H * D
                              : p.ws_o + ((int64_t)qi * p.S + s) * p.H * D;
-    for (int i = tid; i < HWG * C16; i += NT) {
+    constexpr int NIT = HWG * C16 / NT;
+    static_assert(HWG * C16 % NT == 0, "whole rows per pass");
+    u32x4_t v[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int i = it * NT + tid;
+        v[it] = *(const LDS_AS u32x4_t *)(stage_out + (i / C16) * (D * 2) + (i % C16) * 16);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int i = it * NT + tid;
         const int r = i / C16, pos = i % C16;
-        const u32x4_t v = *(const LDS_AS u32x4_t *)(stage_out + r * (D * 2) + pos * 16);
         if (hbase + r < p.H)
-            *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v;
+            *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v[it];
     }
 }
 
@@ -331,7 +341,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][KC * RS];
     __shared__ __attribute__((aligned(16))) f32x4_t xbuf[NW][2 * HT][64];  // partial scores
     __shared__ int32_t list[LIST_CAP];
-    __shared__ int32_t cnt[8 * NW];
+    __shared__ int32_t cnt[NW];
 
     const int bid = blockIdx.x;
     const int unit = unit_of(bid, p.units, p.bs);
@@ -592,7 +602,6 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 //     (compacted in place, sized by K in dynamic LDS) take about 75 KB of
 //     LDS, so two workgroups share a compute unit and one's softmax,
 //     barriers, prologue and epilogue overlap the other's MFMAs.
-// q is staged in the ring in the prologue (padded rows, one head per row).
 template <int D, int NHQ>
 __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) {
     constexpr int HT = 2;                  // head tiles per pair
@@ -607,13 +616,12 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     constexpr int DS = D / 32;             // MFMA k-steps over d
     constexpr int DTH = D / 32;            // 16-wide output tiles in one half of d
     static_assert(KC % NW == 0 && IPW <= 63, "ring shape");
-    static_assert(NW * 16 * RS <= NB * KC * RS, "q of the workgroup fits the ring");
     static_assert(NHQ * HP * D * 2 <= NB * KC * RS, "output staging fits in the ring");
 
     __shared__ __attribute__((aligned(16))) uint8_t tile[NB][KC * RS];
     __shared__ __attribute__((aligned(16))) u32x4_t xp[NW][64];  // bf16 weights of the tile
     __shared__ float xa[NW][64];                                  // rescale factor / final state
-    __shared__ int32_t cnt[8 * NW];
+    __shared__ int32_t cnt[NW];
     extern __shared__ int32_t list[];  // K entries: raw, then compacted in place
 
     const int bid = blockIdx.x;
@@ -631,24 +639,13 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     const int hown = hg * (NHQ * HP) + hq * HP + 16 * w + li;  // head of this lane's scores
     const uint16_t *kvb = p.kv + (int64_t)b * p.N * D;
 
-    // Prologue: the raw list into `list`, this wave's 16 q rows (whole d,
-    // head hh at qstage + hh*RS) into the ring, both by LDS-DMA.
+    // Prologue: the raw list into `list` by LDS-DMA.
     {
         const int32_t *lst = p.idxs + (int64_t)qi * p.K;
         const int NI = (p.K + 63) / 64;
         for (int i = wid; i < NI; i += NW) {
             const int k = i * 64 + lane;
             if (k < p.K) lds_dma4(lst + k, (LDS_AS int32_t *)list + i * 64);
-        }
-    }
-    LDS_AS uint8_t *qstage = (LDS_AS uint8_t *)&tile[0][0] + wid * (16 * RS);
-    {
-        const int h0 = hown - li;
-#pragma unroll
-        for (int hh = 0; hh < 16; ++hh) {
-            const int hsrc = h0 + hh < p.H ? h0 + hh : 0;  // zeroed below
-            if (CPR == 64 || lane < CPR)
-                lds_dma16(p.q + ((int64_t)qi * p.H + hsrc) * D + lane * 8, qstage + hh * RS);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -659,19 +656,6 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     const int lo = (int)(((int64_t)n * s) / p.S);
     const int hi = (int)(((int64_t)n * (s + 1)) / p.S);
     const int nchunks = (hi - lo + KC - 1) / KC;
-
-    // a3: qf[k] = q[hown, 32k + 8g .. +7], the B operands over the whole of d
-    bf16x8_t qf[DS];
-    {
-        const bool ok = hown < p.H;
-#pragma unroll
-        for (int k = 0; k < DS; ++k) {
-            u32x4_t v = *(const LDS_AS u32x4_t *)(qstage + li * RS + (4 * k + g) * 16);
-            if (!ok) v = u32x4_t{0, 0, 0, 0};
-            qf[k] = __builtin_bit_cast(bf16x8_t, v);
-        }
-    }
-    __syncthreads();  // q is in registers: the ring is free
 
     // a2: chunk c (KC rows) into ring slot c % NB, one row per DMA
     // instruction (row r = k*NW + wid for the wave's k-th); tail slots repeat
@@ -695,8 +679,19 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     };
     int next_rows = 0;
     if (nchunks > 0) stage(0, rows_of(0));
-    if (nchunks > 1) stage(1, rows_of(1));
-    if (nchunks > 2) next_rows = rows_of(2);
+    if (nchunks > 1) next_rows = rows_of(1);
+
+    // a3: qf[k] = q[hown, 32k + 8g .. +7], the B operands over the whole of
+    // d, loaded straight into registers while chunk 0 is in flight.  Heads
+    // beyond H read head 0: their scores, weights and accumulators only feed
+    // their own output rows, which are never stored.  The first wait of the
+    // loop (for chunk 0) covers these loads too.
+    bf16x8_t qf[DS];
+    {
+        const uint16_t *qrow = p.q + ((int64_t)qi * p.H + (hown < p.H ? hown : 0)) * D + 8 * g;
+#pragma unroll
+        for (int k = 0; k < DS; ++k) qf[k] = *(const bf16x8_t *)(qrow + 32 * k);
+    }
 
     float m = -INFINITY, lsum = 0.f;  // softmax state of head hown (log2 units)
     f32x4_t o[HT][DTH];               // O^T of both tiles over this wave's half of d
@@ -707,12 +702,16 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 
     for (int c = 0; c < nchunks; ++c) {
         // chunk c has landed once at most the chunk after it is pending
-        wait_vm_ahead<IPW, 1>(c == 0 && nchunks > 1 ? 1 : 0);
+        // Chunk c (and, before the first chunk, q) is the only load in flight.
+        // The wait goes through the builtin so the compiler knows q has
+        // landed; otherwise it would wait for q's loads inside the MFMA
+        // sequence, which also drains the next chunk's DMAs issued there.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
         // chunk c + 1 goes into the slot chunk c - 1 left; its DMAs are spread
         // through the QK^T MFMAs below, so that a wave never waits for a burst
         // of them to be accepted
-        const bool do_stage = c >= 1 && c + 1 < nchunks;
+        const bool do_stage = c + 1 < nchunks;
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NB][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
