@@ -112,6 +112,14 @@ int sparse_attn_fwd_combine(const float *sink, void *out, const sa_dims *d, int3
 int sparse_attn_check_idxs(const int32_t *idxs, const sa_dims *d, int32_t *d_bad_count,
                            hipStream_t stream);
 
+/* Name of the attention kernel a call with these dims and num_splits (0 =
+ * planned) launches on the current device, as profilers list it (static
+ * text), or NULL on bad arguments or a failed device query.  Launches of at
+ * least two workgroups per compute unit take the many-query kernel (two
+ * workgroups share a unit); smaller ones the deep-gather kernel.  For
+ * profiling and reports; no call needs it. */
+const char *sparse_attn_plan_kernel(const sa_dims *d, int32_t num_splits);
+
 /* Static text for a status code (never NULL). */
 const char *sparse_attn_status_str(int status);
 

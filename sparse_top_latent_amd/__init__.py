@@ -5,7 +5,7 @@ package holds the thin binding (``api``), the in-tree build (``build``) and
 the seeded input generators (``workloads``).
 """
 __all__ = ["sparse_attn", "sparse_attn_partial", "sparse_attn_combine", "check_idxs",
-           "plan_splits", "workspace_bytes"]
+           "plan_splits", "plan_kernel", "workspace_bytes"]
 
 
 def __getattr__(name):

@@ -18,6 +18,7 @@ SYMBOLS = (
     "sparse_attn_fwd_partial",
     "sparse_attn_fwd_combine",
     "sparse_attn_check_idxs",
+    "sparse_attn_plan_kernel",
     "sparse_attn_status_str",
 )
 
@@ -56,6 +57,8 @@ def lib():
         L.sparse_attn_fwd_combine.restype = ctypes.c_int
         L.sparse_attn_check_idxs.argtypes = [P, D, P, P]
         L.sparse_attn_check_idxs.restype = ctypes.c_int
+        L.sparse_attn_plan_kernel.argtypes = [D, I32]
+        L.sparse_attn_plan_kernel.restype = ctypes.c_char_p
         L.sparse_attn_status_str.argtypes = [ctypes.c_int]
         L.sparse_attn_status_str.restype = ctypes.c_char_p
         _lib = L

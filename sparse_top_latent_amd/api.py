@@ -62,6 +62,15 @@ def plan_splits(q, kv, idxs) -> int:
     return int(r)
 
 
+def plan_kernel(q, kv, idxs, num_splits: int = 0) -> str:
+    """Name of the attention kernel a call would launch (for reports)."""
+    with torch.cuda.device(q.device):
+        r = _lib.lib().sparse_attn_plan_kernel(ctypes.byref(_dims(q, kv, idxs)), num_splits)
+    if r is None:
+        raise RuntimeError("sparse_attn_plan_kernel: bad arguments or device query failed")
+    return r.decode()
+
+
 def workspace_bytes(q, kv, idxs, num_splits: int = 0) -> int:
     with torch.cuda.device(q.device):
         return int(_lib.lib().sparse_attn_workspace_bytes(ctypes.byref(_dims(q, kv, idxs)),

@@ -1247,6 +1247,33 @@ int sparse_attn_check_idxs(const int32_t *idxs, const sa_dims *d, int32_t *d_bad
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
+const char *sparse_attn_plan_kernel(const sa_dims *d, int32_t num_splits) {
+    if (check_dims(d) != SA_OK || num_splits < 0 || num_splits > MAX_SPLITS) return nullptr;
+    int S = num_splits;
+    if (S == 0) {
+        S = plan_splits(d);
+        if (S < 0) return nullptr;
+    }
+    FwdParams p{};
+    p.units = (int32_t)(queries(d) * head_groups(d->H) * S);
+    if (use_mq(p, d->H)) {
+        const bool two = d->H > 32;
+        switch (d->D) {
+            case 128: return two ? "attn_fwd_mq_kernel<128,2>" : "attn_fwd_mq_kernel<128,1>";
+            case 256: return two ? "attn_fwd_mq_kernel<256,2>" : "attn_fwd_mq_kernel<256,1>";
+            default: return two ? "attn_fwd_mq_kernel<512,2>" : "attn_fwd_mq_kernel<512,1>";
+        }
+    }
+    const WgShape w = shape_for(d->H);
+    static const char *names[3][3] = {
+        {"attn_fwd_kernel<128,4,1>", "attn_fwd_kernel<128,1,2>", "attn_fwd_kernel<128,1,1>"},
+        {"attn_fwd_kernel<256,4,1>", "attn_fwd_kernel<256,1,2>", "attn_fwd_kernel<256,1,1>"},
+        {"attn_fwd_kernel<512,4,1>", "attn_fwd_kernel<512,1,2>", "attn_fwd_kernel<512,1,1>"}};
+    const int di = d->D == 128 ? 0 : d->D == 256 ? 1 : 2;
+    const int wi = w.ht == 1 ? (w.nhq == 4 ? 0 : 2) : 1;
+    return names[di][wi];
+}
+
 const char *sparse_attn_status_str(int status) {
     switch (status) {
         case SA_OK: return "ok";

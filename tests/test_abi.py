@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 8
     assert set(names) == set(_lib.SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -131,3 +131,11 @@ def test_binding_refuses_cpu_tensors():
         sparse_attn(q, kv, None, idx, 0.1)
     with pytest.raises(TypeError):
         sparse_attn(q.float(), kv, None, idx, 0.1)
+
+
+def test_plan_kernel_rejects_bad_arguments(L):
+    # argument errors come back as NULL before any device query
+    assert L.sparse_attn_plan_kernel(None, 1) is None
+    assert L.sparse_attn_plan_kernel(dims(D=100), 1) is None
+    assert L.sparse_attn_plan_kernel(dims(), 65) is None
+    assert L.sparse_attn_plan_kernel(dims(), -1) is None

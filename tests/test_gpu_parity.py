@@ -233,6 +233,17 @@ def test_many_query_path(ref, H, D):
     check(ref, w, 0, what=f"many-query H={H} D={D}")
 
 
+def test_plan_kernel_names_the_dispatch():
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    w = wl.make_decode(B=4)
+    q, kv, _, idx = to_dev(w)
+    assert api.plan_kernel(q, kv, idx, 4) == "attn_fwd_kernel<512,4,1>"
+    wm = wl.make_random(212, 2, many_query_T(), 64, 512, 60, 20)
+    q, kv, _, idx = to_dev(wm)
+    assert api.plan_kernel(q, kv, idx, 0) == "attn_fwd_mq_kernel<512,2>"
+
+
 def test_many_query_splits_stress_and_long_lists(ref):
     T = many_query_T()
     w = wl.make_random(210, 2, T, 64, 512, 120, 40, p_unused=0.2)
