@@ -43,6 +43,9 @@ def parse():
                     help="decode (the benchmark line) or another generator name")
     ap.add_argument("--splits", type=int, default=0, help="0 = planned by the library")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-source", action="store_true",
+                    help="also time the step with the window and compressed rows in two "
+                         "buffers (sparse_attn_fwd_2src) and the concatenation it avoids")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run plain 256 MiB copies first (HBM counter calibration)")
     return ap.parse_args()
@@ -229,6 +232,47 @@ def main():
                        "note": "same inputs every step: rows may be served from the Infinity Cache"},
         "roofline": roof,
     }
+
+    if args.two_source:
+        # the rows as the model holds them: window rows and compressed rows in
+        # separate buffers; the one-buffer path needs them concatenated first
+        W = w.window_rows
+        wins = [k[:, :W].contiguous() for k in kvs]
+        cmps = [k[:, W:].contiguous() for k in kvs]
+
+        def step2(i):
+            api.sparse_attn_2src(qs[i], wins[i], cmps[i], W, w.N, sink, idxs[i], w.scale,
+                                 out=out, num_splits=S, workspace=ws)
+
+        def cat(i):
+            torch.cat([wins[i], cmps[i]], dim=1)
+
+        def time_graph(fn):
+            for i in range(R):
+                fn(i)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                for i in range(R):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+            gate(torch)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(1, args.steps // R)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / (reps * R)
+
+        ms2 = time_graph(step2)
+        ms_cat = time_graph(cat)
+        line["two_source"] = {
+            "window_rows": W, "ms_per_step": round(ms2, 5), "value": round(Qn / (ms2 * 1e-3), 1),
+            "concat_copy_ms": round(ms_cat, 5),
+            "note": "rows read in place from the window and compressed buffers; "
+                    "concat_copy_ms is the torch.cat the one-buffer call needs first"}
 
     if not args.no_cpu_baseline:
         import oracle

@@ -93,6 +93,23 @@ int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int3
                     float scale, void *out, const sa_dims *d, int32_t num_splits,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The same step with the rows in two buffers instead of one concatenated kv
+ * (DeepSeek-V4.1 pages, "Output projection" page, Attention.forward excerpt:
+ * kv = cat([window_kv, compress_kv], dim=1), with compressed indices offset by
+ * the window length).  Entry j of a list (0 <= j < N = d->N) addresses
+ *   j <  W : kv_win[b, j, :]        kv_win bf16 [B, win_rows, D], W <= win_rows
+ *   j >= W : kv_cmp[b, j - W, :]    kv_cmp bf16 [B, cmp_rows, D], N - W <= cmp_rows
+ * so a window ring and a compressed cache (with spare rows beyond the filled
+ * length) are read in place, without the copy the concatenation makes.  The
+ * result equals sparse_attn_fwd on the concatenated rows, bit for bit.
+ * kv_win may be NULL when W == 0 and kv_cmp when W == N; both 16-byte aligned.
+ * SA_ERR_SHAPE when W is outside [0, N] or a buffer has too few rows.  Other
+ * arguments, checks and behaviour as sparse_attn_fwd. */
+int sparse_attn_fwd_2src(const void *q, const void *kv_win, int32_t win_rows, const void *kv_cmp,
+                         int32_t cmp_rows, int32_t W, const float *sink, const int32_t *idxs,
+                         float scale, void *out, const sa_dims *d, int32_t num_splits,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* First half of the split path (num_splits >= 2): writes the partials of every
  * split into `workspace` and nothing into out.  Same arguments and checks as
  * sparse_attn_fwd, without out. */

@@ -69,6 +69,21 @@ def sparse_attn_ref(q_bits, kv_bits, sink, idxs, scale, *, weights: bool = False
     return _call(_load(), q_bits, kv_bits, sink, idxs, scale, weights)
 
 
+def sparse_attn_2src_ref(q_bits, win_bits, cmp_bits, W, N, sink, idxs, scale):
+    """The step over rows held in two buffers, as the pages define it: the
+    window rows and the compressed rows are joined along the row axis and the
+    compressed indices are offset by the window length (DeepSeek-V4.1 pages,
+    "Output projection" page, Attention.forward excerpt, the cat of window_kv
+    and compress_kv).  Entry j < W is win_bits[b, j]; j >= W is
+    cmp_bits[b, j - W]; N is the joined row count."""
+    win_bits = np.asarray(win_bits, dtype=np.uint16)
+    cmp_bits = np.asarray(cmp_bits, dtype=np.uint16)
+    if not (0 <= W <= N) or win_bits.shape[1] < W or cmp_bits.shape[1] < N - W:
+        raise ValueError("W outside [0, N] or a buffer with too few rows")
+    kv = np.concatenate([win_bits[:, :W], cmp_bits[:, :N - W]], axis=1)
+    return sparse_attn_ref(q_bits, kv, sink, idxs, scale)
+
+
 def ref_from_library(path):
     """The same interface over another build of the oracle's C entry point
     (the tests use it to run the pins against planted mistakes)."""

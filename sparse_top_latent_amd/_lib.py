@@ -15,6 +15,7 @@ SYMBOLS = (
     "sparse_attn_plan_splits",
     "sparse_attn_workspace_bytes",
     "sparse_attn_fwd",
+    "sparse_attn_fwd_2src",
     "sparse_attn_fwd_partial",
     "sparse_attn_fwd_combine",
     "sparse_attn_check_idxs",
@@ -51,6 +52,8 @@ def lib():
         L.sparse_attn_workspace_bytes.restype = SZ
         L.sparse_attn_fwd.argtypes = [P, P, P, P, F, P, D, I32, P, SZ, P]
         L.sparse_attn_fwd.restype = ctypes.c_int
+        L.sparse_attn_fwd_2src.argtypes = [P, P, I32, P, I32, I32, P, P, F, P, D, I32, P, SZ, P]
+        L.sparse_attn_fwd_2src.restype = ctypes.c_int
         L.sparse_attn_fwd_partial.argtypes = [P, P, P, F, D, I32, P, SZ, P]
         L.sparse_attn_fwd_partial.restype = ctypes.c_int
         L.sparse_attn_fwd_combine.argtypes = [P, P, D, I32, P, SZ, P]

@@ -100,6 +100,34 @@ def sparse_attn(q, kv, sink, idxs, scale: float, out=None, num_splits: int = 0,
     return out
 
 
+def sparse_attn_2src(q, kv_win, kv_cmp, W: int, N: int, sink, idxs, scale: float, out=None,
+                     num_splits: int = 0, workspace=None):
+    """sparse_attn over rows held in two buffers: list entry j < W is kv_win[b, j],
+    j >= W is kv_cmp[b, j - W] (N = the index space, W <= kv_win.shape[1],
+    N - W <= kv_cmp.shape[1]); equal to sparse_attn on the concatenated rows."""
+    B, T, H, D = q.shape
+    for t in (kv_win, kv_cmp):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 3 or t.shape[0] != B \
+                or t.shape[2] != D or t.device != q.device:
+            raise ValueError("kv_win and kv_cmp must be contiguous bf16 [B, rows, D] on q's device")
+    _check_tensors(q, kv_win, sink, idxs)
+    dims = SaDims(B, T, H, D, N, idxs.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    L = _lib.lib()
+    with torch.cuda.device(q.device):
+        need = int(L.sparse_attn_workspace_bytes(ctypes.byref(dims), num_splits))
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = L.sparse_attn_fwd_2src(_ptr(q), _ptr(kv_win), kv_win.shape[1], _ptr(kv_cmp),
+                                    kv_cmp.shape[1], W, _ptr(sink), _ptr(idxs),
+                                    ctypes.c_float(scale), _ptr(out), ctypes.byref(dims),
+                                    num_splits, _ptr(workspace), ws_bytes, _stream(q.device))
+    _lib.check(rc, "sparse_attn_fwd_2src")
+    return out
+
+
 def sparse_attn_partial(q, kv, idxs, scale: float, num_splits: int, workspace):
     """First kernel of the split path: per-split partials into ``workspace``."""
     _check_tensors(q, kv, None, idxs)

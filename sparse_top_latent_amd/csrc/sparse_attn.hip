@@ -52,7 +52,12 @@ constexpr float MAX_SLACK = 8.0f;
 
 struct FwdParams {
     const uint16_t *q;
-    const uint16_t *kv;
+    // Rows: index j < W is row j of the first source (rows_a rows per
+    // sequence), j >= W is row j - W of the second (rows_b per sequence).
+    // One tensor is the case W = N.
+    const uint16_t *kv;     // first source  [B, rows_a, D]
+    const uint16_t *kv2;    // second source [B, rows_b, D]
+    int64_t W, rows_a, rows_b;
     const float *sink;
     const int32_t *idxs;
     uint16_t *out;     // non-split path
@@ -359,7 +364,9 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 
     // head of this lane in head tile t: hw0 + 16 t + li
     const int hw0 = hg * HWG + hq * HW;
-    const uint16_t *kvb = p.kv + (int64_t)b * p.N * D;
+    // row j of this sequence lives at (j < W ? kva : kvb2) + j * D
+    const uint16_t *kva = p.kv + (int64_t)b * p.rows_a * D;
+    const uint16_t *kvb2 = p.kv2 + ((int64_t)b * p.rows_b - p.W) * D;
     static_assert(NBUF == 4, "the prologue stages q in ring slots 1-2 and the list in slot 3");
 
     // Prologue.  The index list and q come in through LDS-DMA too, so every
@@ -430,7 +437,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         for (int k = 0; k < IPW; ++k) {
             const int r = k * NW + wid;
             if (CPR == 64 || lane < CPR)
-                lds_dma16(kvb + (int64_t)row[k] * D + lane * 8,
+                lds_dma16((row[k] < p.W ? kva : kvb2) + (int64_t)row[k] * D + lane * 8,
                           (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS));
         }
     };
@@ -637,7 +644,8 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     const int w = wid & 1;        // own head tile (QK^T, softmax) and half of d (PV)
     const int g = lane >> 4, li = lane & 15;
     const int hown = hg * (NHQ * HP) + hq * HP + 16 * w + li;  // head of this lane's scores
-    const uint16_t *kvb = p.kv + (int64_t)b * p.N * D;
+    const uint16_t *kva = p.kv + (int64_t)b * p.rows_a * D;          // rows j < W
+    const uint16_t *kvb2 = p.kv2 + ((int64_t)b * p.rows_b - p.W) * D;  // rows j >= W
 
     // Prologue: the raw list into `list` by LDS-DMA.
     {
@@ -670,7 +678,7 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     auto stage_one = [&](int c, int rows, int k) {  // this wave's k-th row of chunk c
         LDS_AS uint8_t *buf = (LDS_AS uint8_t *)&tile[c % NB][0];
         const int row = __builtin_amdgcn_readlane(rows, k);
-        const uint16_t *src = kvb + (int64_t)row * D;
+        const uint16_t *src = (row < p.W ? kva : kvb2) + (int64_t)row * D;
         if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, buf + (k * NW + wid) * RS);
     };
     auto stage = [&](int c, int rows) {
@@ -1099,6 +1107,10 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
     FwdParams p{};
     p.q = (const uint16_t *)q;
     p.kv = (const uint16_t *)kv;
+    p.kv2 = (const uint16_t *)kv;
+    p.W = d->N;
+    p.rows_a = d->N;
+    p.rows_b = 0;
     p.sink = sink;
     p.idxs = idxs;
     p.out = (uint16_t *)out;
@@ -1198,6 +1210,36 @@ int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int3
     if (!aligned(out, 16) || !aligned(sink, 4)) return SA_ERR_ALIGN;
     if (!units_fit(d, S)) return SA_ERR_SHAPE;
     const FwdParams p = make_params(q, kv, sink, idxs, scale, out, d, S, workspace);
+    if (run_fwd(p, d->D, d->H, stream) != hipSuccess) return SA_ERR_HIP;
+    if (S > 1 && launch_combine(d, S, sink, out, workspace, ws_layout(d, S), stream) != hipSuccess)
+        return SA_ERR_HIP;
+    return SA_OK;
+}
+
+int sparse_attn_fwd_2src(const void *q, const void *kv_win, int32_t win_rows, const void *kv_cmp,
+                         int32_t cmp_rows, int32_t W, const float *sink, const int32_t *idxs,
+                         float scale, void *out, const sa_dims *d, int32_t num_splits,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_dims(d);
+    if (rc != SA_OK) return rc;
+    if (W < 0 || W > d->N || win_rows < W || cmp_rows < d->N - W) return SA_ERR_SHAPE;
+    if (queries(d) == 0) return num_splits < 0 || num_splits > MAX_SPLITS ? SA_ERR_SPLITS : SA_OK;
+    if ((W > 0 && kv_win == nullptr) || (d->N > W && kv_cmp == nullptr)) return SA_ERR_NULL;
+    if (!aligned(kv_win, 16) || !aligned(kv_cmp, 16)) return SA_ERR_ALIGN;
+    // the common checks see one non-null source; both were checked above
+    const void *any = W > 0 ? kv_win : (d->N > W ? kv_cmp : q);
+    int S = 1;
+    rc = check_common(q, any, idxs, d, num_splits, workspace, workspace_bytes, false, &S);
+    if (rc != SA_OK) return rc;
+    if (out == nullptr) return SA_ERR_NULL;
+    if (!aligned(out, 16) || !aligned(sink, 4)) return SA_ERR_ALIGN;
+    if (!units_fit(d, S)) return SA_ERR_SHAPE;
+    FwdParams p = make_params(q, any, sink, idxs, scale, out, d, S, workspace);
+    p.kv = (const uint16_t *)(kv_win != nullptr ? kv_win : any);
+    p.kv2 = (const uint16_t *)(kv_cmp != nullptr ? kv_cmp : any);
+    p.W = W;
+    p.rows_a = win_rows;
+    p.rows_b = cmp_rows;
     if (run_fwd(p, d->D, d->H, stream) != hipSuccess) return SA_ERR_HIP;
     if (S > 1 && launch_combine(d, S, sink, out, workspace, ws_layout(d, S), stream) != hipSuccess)
         return SA_ERR_HIP;

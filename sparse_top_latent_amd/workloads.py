@@ -66,6 +66,7 @@ class Workload:
     idxs: np.ndarray                 # int32 [B, T, K]
     sink: np.ndarray                 # float32 [H]
     q: np.ndarray                    # uint16 bf16 bits [B, T, H, D]
+    window_rows: int = 0             # rows [0, window_rows) are the window (raw or ring) rows
     rows: list = field(default_factory=list)   # per b: int64 sorted referenced row ids
     vals: list = field(default_factory=list)   # per b: uint16 [len(rows[b]), D]
 
@@ -119,7 +120,7 @@ class Workload:
         return 4 * self.H * self.D * self.valid_entries()
 
 
-def _finish(name, B, T, H, D, N, K, scale, seed, idxs) -> Workload:
+def _finish(name, B, T, H, D, N, K, scale, seed, idxs, window_rows=None) -> Workload:
     idxs = np.ascontiguousarray(idxs, dtype=np.int32)
     sink = _rng(seed, 1).standard_normal(H, dtype=np.float32)
     q = to_bf16_bits(_rng(seed, 2).standard_normal((B, T, H, D), dtype=np.float32))
@@ -129,7 +130,8 @@ def _finish(name, B, T, H, D, N, K, scale, seed, idxs) -> Workload:
         r = np.unique(idxs[b][idxs[b] >= 0]).astype(np.int64)
         rows.append(r)
         vals.append(to_bf16_bits(kv_rng.standard_normal((len(r), D), dtype=np.float32)))
-    return Workload(name, B, T, H, D, N, K, scale, seed, idxs, sink, q, rows, vals)
+    return Workload(name, B, T, H, D, N, K, scale, seed, idxs, sink, q,
+                    N if window_rows is None else window_rows, rows, vals)
 
 
 def make_tiny(seed: int = CONFIG_SEEDS["tiny"]) -> Workload:
@@ -148,7 +150,7 @@ def make_tiny(seed: int = CONFIG_SEEDS["tiny"]) -> Workload:
         idxs[0, t, W:] = W + rng.choice(C, 8, replace=False)
     drop = rng.random((B, T, K)) < 0.1
     idxs[drop] = -1
-    return _finish("tiny", B, T, H, D, W + C, K, D ** -0.5, seed, idxs)
+    return _finish("tiny", B, T, H, D, W + C, K, D ** -0.5, seed, idxs, W)
 
 
 def make_decode(seed: int = CONFIG_SEEDS["decode"], B: int = 64, H: int = 64,
@@ -164,7 +166,7 @@ def make_decode(seed: int = CONFIG_SEEDS["decode"], B: int = 64, H: int = 64,
     for b in range(B):
         idxs[b, 0, :W] = np.arange(W)
         idxs[b, 0, W:] = W + rng.choice(C, 512, replace=False)
-    return _finish("decode", B, 1, H, D, W + C, K, 512 ** -0.5, seed, idxs)
+    return _finish("decode", B, 1, H, D, W + C, K, 512 ** -0.5, seed, idxs, W)
 
 
 def make_prefill(seed: int = CONFIG_SEEDS["prefill"], T: int = 4096, H: int = 64,
@@ -187,7 +189,7 @@ def make_prefill(seed: int = CONFIG_SEEDS["prefill"], T: int = 4096, H: int = 64
         n_c = min(512, vis)
         if n_c:
             idxs[0, t, W:W + n_c] = T + rng.choice(vis, n_c, replace=False)
-    return _finish("prefill", 1, T, H, D, T + C, K, 512 ** -0.5, seed, idxs)
+    return _finish("prefill", 1, T, H, D, T + C, K, 512 ** -0.5, seed, idxs, T)
 
 
 def make_long(seed: int = CONFIG_SEEDS["long"], B: int = 32, H: int = 64,
@@ -208,7 +210,7 @@ def make_long(seed: int = CONFIG_SEEDS["long"], B: int = 32, H: int = 64,
                 offs.append(o)
         idxs[b, 0, :W] = np.arange(W)
         idxs[b, 0, W:] = np.concatenate([W + o + np.arange(run_len) for o in offs])
-    return _finish("long", B, 1, H, D, W + C, K, 512 ** -0.5, seed, idxs)
+    return _finish("long", B, 1, H, D, W + C, K, 512 ** -0.5, seed, idxs, W)
 
 
 def make_ragged(seed: int = CONFIG_SEEDS["ragged"], B: int = 256, H: int = 64,
@@ -228,7 +230,7 @@ def make_ragged(seed: int = CONFIG_SEEDS["ragged"], B: int = 256, H: int = 64,
         n_c = min(512, vis)
         idxs[b, 0, :W] = np.arange(W)
         idxs[b, 0, W:W + n_c] = W + rng.choice(vis, n_c, replace=False)
-    return _finish("ragged", B, 1, H, D, W + Cmax, K, 512 ** -0.5, seed, idxs)
+    return _finish("ragged", B, 1, H, D, W + Cmax, K, 512 ** -0.5, seed, idxs, W)
 
 
 def make_window(seed: int = CONFIG_SEEDS["window"], B: int = 64, H: int = 64,

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     assert set(names) == set(_lib.SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -139,3 +139,25 @@ def test_plan_kernel_rejects_bad_arguments(L):
     assert L.sparse_attn_plan_kernel(dims(D=100), 1) is None
     assert L.sparse_attn_plan_kernel(dims(), 65) is None
     assert L.sparse_attn_plan_kernel(dims(), -1) is None
+
+
+def fwd2(L, q=A, win=A, win_rows=100, cmp=A, cmp_rows=100, W=40, d=None, S=1):
+    return L.sparse_attn_fwd_2src(q, win, win_rows, cmp, cmp_rows, W, None, A,
+                                  ctypes.c_float(0.1), A2, dims() if d is None else d, S, None,
+                                  0, None)
+
+
+def test_two_source_argument_errors(L):
+    # dims() has N=100: entries j < W come from the window buffer, j >= W from
+    # the compressed one; every error is reported before any HIP call
+    assert fwd2(L, W=-1) == SA_ERR_SHAPE
+    assert fwd2(L, W=101) == SA_ERR_SHAPE
+    assert fwd2(L, W=40, win_rows=39) == SA_ERR_SHAPE          # window buffer too short
+    assert fwd2(L, W=40, cmp_rows=59) == SA_ERR_SHAPE          # compressed buffer too short
+    assert fwd2(L, W=40, win=None) == SA_ERR_NULL
+    assert fwd2(L, W=40, cmp=None) == SA_ERR_NULL
+    assert fwd2(L, W=40, win=ctypes.c_void_p(0x10008)) == SA_ERR_ALIGN
+    assert fwd2(L, W=40, S=65) == SA_ERR_SPLITS
+    assert fwd2(L, d=dims(D=100)) == SA_ERR_UNSUPPORTED
+    # a NULL buffer that no entry can address is fine; zero queries is a no-op
+    assert fwd2(L, q=None, win=None, cmp=None, d=dims(B=0), W=0) == SA_OK

@@ -260,6 +260,72 @@ def test_many_query_splits_stress_and_long_lists(ref):
     check(ref, wl2, 0, what="many-query K=2048")
 
 
+# ------------------------------------------------- two-source rows (window + compressed)
+
+def split_sources(w, W, spare=(3, 5)):
+    """The workload's rows as two buffers with NaN spare rows: window rows
+    [0, W) and compressed rows [W, N) (host bits and device tensors)."""
+    torch = torch_mod()
+    kvh = w.kv_host()
+    nan = np.uint16(0x7FC0)
+    win_h = np.full((w.B, W + spare[0], w.D), nan, np.uint16)
+    cmp_h = np.full((w.B, w.N - W + spare[1], w.D), nan, np.uint16)
+    win_h[:, :W] = kvh[:, :W]
+    cmp_h[:, :w.N - W] = kvh[:, W:]
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return win_h, cmp_h, dev(win_h), dev(cmp_h)
+
+
+def check_two_source(ref2, w, W, S, what):
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    q, kv, sk, idx = to_dev(w)
+    win_h, cmp_h, win, cmp_ = split_sources(w, W)
+    one = api.sparse_attn(q, kv, sk, idx, w.scale, num_splits=S)
+    two = api.sparse_attn_2src(q, win, cmp_, W, w.N, sk, idx, w.scale, num_splits=S)
+    torch.cuda.synchronize()
+    # the same rows in the same order: bit for bit the one-buffer result
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16)), f"{what}: differs from one buffer"
+    got = wl.bf16_bits_to_f32(two.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    exp = ref2(w.q, win_h, cmp_h, W, w.N, w.sink, w.idxs, w.scale)
+    assert_close(got, exp, what)
+
+
+@pytest.fixture(scope="module")
+def ref2():
+    import oracle
+    oracle.build(force=False)
+    return oracle.sparse_attn_2src_ref
+
+
+@pytest.mark.parametrize("W", [0, 128, 300])
+@pytest.mark.parametrize("S", [1, 3])
+def test_two_source_rows(ref2, W, S):
+    w = wl.make_random(220, 2, 3, 64, 512, 300, 173, p_unused=0.3)
+    check_two_source(ref2, w, W, S, f"two-source W={W} S={S}")
+
+
+def test_two_source_many_query_path(ref2):
+    w = wl.make_random(221, 2, many_query_T(), 64, 512, 160, 75, p_unused=0.3)
+    check_two_source(ref2, w, 40, 0, "two-source many-query W=40")
+
+
+def test_two_source_full_decode():
+    # the decode shape as the model holds it: a 128-row window ring and the
+    # compressed cache; bit for bit the one-buffer result on every query
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    w = wl.make("decode")
+    q, kv, sk, idx = to_dev(w)
+    win = kv[:, :128].contiguous()
+    cmp_ = torch.full((w.B, w.N - 128 + 64, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    cmp_[:, :w.N - 128] = kv[:, 128:]
+    one = api.sparse_attn(q, kv, sk, idx, w.scale)
+    two = api.sparse_attn_2src(q, win, cmp_, 128, w.N, sk, idx, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+
+
 # --------------------------------------------------------- full-size workloads
 # Same launch configuration as bench.py: num_splits=0 (planned by the library).
 

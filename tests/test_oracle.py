@@ -35,3 +35,55 @@ def test_any_negative_index_is_unused(ref):
     other = np.where(w.idxs < 0, -7, w.idxs).astype(np.int32)
     np.testing.assert_array_equal(ref(w.q, kv, w.sink, w.idxs, w.scale),
                                   ref(w.q, kv, w.sink, other, w.scale))
+
+
+def per_entry_two_source(q_bits, win_bits, cmp_bits, W, sink, idxs, scale):
+    """Brute force written from the two-source rule itself: every list entry is
+    resolved to its buffer one at a time (j < W: window row j; else compressed
+    row j - W), then the sink softmax is taken directly in float64."""
+    from sparse_top_latent_amd.workloads import bf16_bits_to_f32
+    q = bf16_bits_to_f32(q_bits).astype(np.float64)
+    win = bf16_bits_to_f32(win_bits).astype(np.float64)
+    cmp_ = bf16_bits_to_f32(cmp_bits).astype(np.float64)
+    B, T, H, D = q.shape
+    sc = float(np.float32(scale))
+    out = np.zeros((B, T, H, D))
+    for b in range(B):
+        for t in range(T):
+            rows = [win[b, j] if j < W else cmp_[b, j - W] for j in idxs[b, t] if j >= 0]
+            if not rows:
+                continue
+            R = np.stack(rows)
+            for h in range(H):
+                z = sc * (R @ q[b, t, h])
+                logits = np.concatenate([z, [float(sink[h])]])
+                m = logits.max()
+                e = np.exp(logits - m)
+                out[b, t, h] = (e[:-1] @ R) / e.sum()
+    return out
+
+
+def test_two_source_oracle_pinned():
+    """The two-source oracle (rows joined as the pages join window and
+    compressed rows) against a per-entry brute force, on buffers with spare
+    rows, and its reductions to one buffer (W = N and W = 0)."""
+    import oracle
+    oracle.build(force=False)
+    rng = np.random.default_rng(7)
+    from sparse_top_latent_amd.workloads import to_bf16_bits
+    B, T, H, D, W, C, K = 2, 3, 4, 16, 5, 9, 10
+    q = to_bf16_bits(rng.standard_normal((B, T, H, D), dtype=np.float32))
+    win = to_bf16_bits(rng.standard_normal((B, W + 2, D), dtype=np.float32))   # 2 spare rows
+    cmp_ = to_bf16_bits(rng.standard_normal((B, C + 3, D), dtype=np.float32))  # 3 spare rows
+    sink = rng.standard_normal(H).astype(np.float32)
+    idxs = rng.integers(-1, W + C, (B, T, K)).astype(np.int32)
+    idxs[0, 0, :3] = [0, W - 1, W]          # both edges of the split
+    got = oracle.sparse_attn_2src_ref(q, win, cmp_, W, W + C, sink, idxs, 0.3)
+    exp = per_entry_two_source(q, win, cmp_, W, sink, idxs, 0.3)
+    assert np.max(np.abs(got - exp)) < 1e-12
+    one = oracle.sparse_attn_ref(q, win[:, :W], sink, np.where(idxs < W, idxs, -1), 0.3)
+    assert np.array_equal(oracle.sparse_attn_2src_ref(q, win, cmp_, W, W, sink,
+                                                      np.where(idxs < W, idxs, -1), 0.3), one)
+    zero = oracle.sparse_attn_ref(q, cmp_[:, :C], sink, np.where(idxs < C, idxs, -1), 0.3)
+    assert np.array_equal(oracle.sparse_attn_2src_ref(q, win, cmp_, 0, C, sink,
+                                                      np.where(idxs < C, idxs, -1), 0.3), zero)
