@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--two-source", action="store_true",
                     help="also time the step with the window and compressed rows in two "
                          "buffers (sparse_attn_fwd_2src) and the concatenation it avoids")
+    ap.add_argument("--kv-format", default="bf16", choices=["bf16", "fp4"],
+                    help="fp4: also time the step with the compressed rows packed as FP4 "
+                         "records (E2M1 codes, one E4M3 scale per 16) beside bf16 window rows")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run plain 256 MiB copies first (HBM counter calibration)")
     return ap.parse_args()
@@ -273,6 +276,48 @@ def main():
             "concat_copy_ms": round(ms_cat, 5),
             "note": "rows read in place from the window and compressed buffers; "
                     "concat_copy_ms is the torch.cat the one-buffer call needs first"}
+
+    if args.kv_format == "fp4":
+        # window rows bf16, compressed rows as packed FP4 records (the pages'
+        # cache format); synthetic records, the same index lists
+        W = w.window_rows
+        Rb = api.fp4_record_bytes(w.D)
+        rec0 = torch.from_numpy(wl.make_fp4_records(w.seed, w.B, w.N - W, w.D, Rb)).to(dev)
+        recs = [rec0] + [rec0.clone() for _ in range(R - 1)]
+        wins4 = [k[:, :W].contiguous() for k in kvs]
+
+        def step4(i):
+            api.sparse_attn_2src_fp4(qs[i], wins4[i], recs[i], W, w.N, sink, idxs[i], w.scale,
+                                     out=out, num_splits=S, workspace=ws)
+
+        for i in range(R):
+            step4(i)
+        g4 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g4, stream=cap_stream):
+            for i in range(R):
+                step4(i)
+        g4.replay()
+        torch.cuda.synchronize()
+        gate(torch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.steps // R)
+        e0.record()
+        for _ in range(reps):
+            g4.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms4 = e0.elapsed_time(e1) / (reps * R)
+        # algorithmic bytes: distinct window rows x 2D + distinct compressed rows x record
+        nwin = sum(int(np.count_nonzero(np.asarray(r) < W)) for r in w.rows)
+        ncmp = sum(int(np.count_nonzero(np.asarray(r) >= W)) for r in w.rows)
+        b4 = (nwin * w.D * 2 + ncmp * Rb + 2 * Qn * w.H * w.D * 2 + w.idxs.size * 4 + w.H * 4)
+        t4 = max(b4 / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+        line["kv_fp4"] = {
+            "ms_per_step": round(ms4, 5), "value": round(Qn / (ms4 * 1e-3), 1),
+            "record_bytes": Rb, "algorithmic_bytes": b4,
+            "path_roofline_frac": round(t4 / (ms4 * 1e-3), 4),
+            "note": "window rows bf16; compressed rows as FP4 records (E2M1 codes + one E4M3 "
+                    "scale per 16 elements), expanded to bf16 in LDS"}
 
     if not args.no_cpu_baseline:
         import oracle

@@ -110,6 +110,27 @@ int sparse_attn_fwd_2src(const void *q, const void *kv_win, int32_t win_rows, co
                          float scale, void *out, const sa_dims *d, int32_t num_splits,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of one packed FP4 row record for head dimension D (D/2 code bytes +
+ * D/16 scale bytes, rounded up to 16): 288 at D = 512.  0 for an unsupported D. */
+int32_t sparse_attn_fp4_record_bytes(int32_t D);
+
+/* sparse_attn_fwd_2src with the compressed rows packed as the pages' cache
+ * quantises them (DeepSeek-V4.1 pages, "blocks, re-index groups" page,
+ * compressor excerpt: groups of 16 elements, FP4 values with E4M3 scales).
+ * cmp_records holds one record of R = sparse_attn_fp4_record_bytes(D) bytes per
+ * row, [B, cmp_rows, R], 16-byte aligned: bytes 0 .. D/2-1 are OCP E2M1 codes
+ * (byte k: element 2k in the low nibble, element 2k+1 in the high nibble),
+ * bytes D/2 .. D/2 + D/16 - 1 are OCP E4M3 scales (scale g for elements
+ * 16g .. 16g+15), the rest is padding.  Element i of the row is
+ * E2M1(code i) x E4M3(scale i/16); the product is exact in bf16, and the result
+ * equals sparse_attn_fwd_2src on those bf16 rows, bit for bit.  The window rows
+ * stay bf16.  A NaN scale code makes its group NaN. */
+int sparse_attn_fwd_2src_fp4(const void *q, const void *kv_win, int32_t win_rows,
+                             const void *cmp_records, int32_t cmp_rows, int32_t W,
+                             const float *sink, const int32_t *idxs, float scale, void *out,
+                             const sa_dims *d, int32_t num_splits, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 /* First half of the split path (num_splits >= 2): writes the partials of every
  * split into `workspace` and nothing into out.  Same arguments and checks as
  * sparse_attn_fwd, without out. */

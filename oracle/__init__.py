@@ -84,6 +84,64 @@ def sparse_attn_2src_ref(q_bits, win_bits, cmp_bits, W, N, sink, idxs, scale):
     return sparse_attn_ref(q_bits, kv, sink, idxs, scale)
 
 
+def e2m1_values(codes):
+    """OCP MX FP4 (E2M1): bit 3 sign, bits 2-1 exponent with bias 1, bit 0
+    mantissa; exponent 0 is subnormal (0 or 0.5).  The pages name FP4 for the
+    compressed cache (DeepSeek-V4.1 pages, "blocks, re-index groups" page,
+    compressor excerpt, fp4_act_quant with groups of 16)."""
+    c = np.asarray(codes, dtype=np.int64)
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, np.maximum(e - 1, 0)))
+    return np.where(c & 8, -mag, mag)
+
+
+def e4m3_values(codes):
+    """OCP FP8 E4M3 (float8_e4m3fn, the scale dtype of the same excerpt): bit 7
+    sign, bits 6-3 exponent with bias 7, bits 2-0 mantissa; exponent 0 is
+    subnormal (m * 2^-9); 0x7F and 0xFF are NaN; no infinities."""
+    c = np.asarray(codes, dtype=np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def fp4_records_to_rows(records, D):
+    """Packed FP4 row records [.., R] -> float64 rows [.., D]: bytes 0..D/2-1
+    hold the E2M1 codes (byte k: element 2k in the low nibble, 2k+1 in the high
+    nibble), bytes D/2..D/2+D/16-1 the E4M3 scales of the groups of 16."""
+    rec = np.asarray(records, dtype=np.uint8)
+    codes = rec[..., :D // 2].astype(np.int64)
+    el = np.stack([codes & 15, codes >> 4], axis=-1).reshape(*rec.shape[:-1], D)
+    scales = e4m3_values(rec[..., D // 2:D // 2 + D // 16])
+    return e2m1_values(el) * np.repeat(scales, 16, axis=-1)
+
+
+def _f64_to_bf16_bits_exact(x):
+    """float64 values that bf16 holds exactly (or NaN) -> bf16 bit patterns."""
+    f = np.asarray(x, dtype=np.float32)
+    if not np.array_equal(f.astype(np.float64), np.asarray(x, np.float64), equal_nan=True):
+        raise ValueError("value not exact in float32")
+    bits = f.view(np.uint32)
+    nan = np.isnan(f)
+    if np.any((bits & 0xFFFF)[~nan] != 0):
+        raise ValueError("value not exact in bf16")
+    return np.where(nan, np.uint16(0x7FC0), (bits >> 16).astype(np.uint16)).astype(np.uint16)
+
+
+def sparse_attn_2src_fp4_ref(q_bits, win_bits, records, W, N, sink, idxs, scale):
+    """The two-source step with the compressed rows given as packed FP4 records:
+    each record is decoded to its exact values (E2M1 code times the E4M3 scale
+    of its group of 16; exact in bf16), then the step is the same as for
+    bf16 rows."""
+    D = np.asarray(q_bits).shape[-1]
+    rows = fp4_records_to_rows(records, D)
+    return sparse_attn_2src_ref(q_bits, win_bits, _f64_to_bf16_bits_exact(rows), W, N, sink,
+                                idxs, scale)
+
+
 def ref_from_library(path):
     """The same interface over another build of the oracle's C entry point
     (the tests use it to run the pins against planted mistakes)."""

@@ -16,6 +16,8 @@ SYMBOLS = (
     "sparse_attn_workspace_bytes",
     "sparse_attn_fwd",
     "sparse_attn_fwd_2src",
+    "sparse_attn_fwd_2src_fp4",
+    "sparse_attn_fp4_record_bytes",
     "sparse_attn_fwd_partial",
     "sparse_attn_fwd_combine",
     "sparse_attn_check_idxs",
@@ -54,6 +56,10 @@ def lib():
         L.sparse_attn_fwd.restype = ctypes.c_int
         L.sparse_attn_fwd_2src.argtypes = [P, P, I32, P, I32, I32, P, P, F, P, D, I32, P, SZ, P]
         L.sparse_attn_fwd_2src.restype = ctypes.c_int
+        L.sparse_attn_fwd_2src_fp4.argtypes = [P, P, I32, P, I32, I32, P, P, F, P, D, I32, P, SZ, P]
+        L.sparse_attn_fwd_2src_fp4.restype = ctypes.c_int
+        L.sparse_attn_fp4_record_bytes.argtypes = [I32]
+        L.sparse_attn_fp4_record_bytes.restype = I32
         L.sparse_attn_fwd_partial.argtypes = [P, P, P, F, D, I32, P, SZ, P]
         L.sparse_attn_fwd_partial.restype = ctypes.c_int
         L.sparse_attn_fwd_combine.argtypes = [P, P, D, I32, P, SZ, P]

@@ -128,6 +128,43 @@ def sparse_attn_2src(q, kv_win, kv_cmp, W: int, N: int, sink, idxs, scale: float
     return out
 
 
+def fp4_record_bytes(D: int) -> int:
+    """Bytes of one packed FP4 compressed-row record (288 at D = 512)."""
+    return int(_lib.lib().sparse_attn_fp4_record_bytes(D))
+
+
+def sparse_attn_2src_fp4(q, kv_win, cmp_records, W: int, N: int, sink, idxs, scale: float,
+                         out=None, num_splits: int = 0, workspace=None):
+    """sparse_attn_2src with the compressed rows as packed FP4 records
+    (uint8 [B, rows, fp4_record_bytes(D)]): E2M1 codes and one E4M3 scale per 16
+    elements; equal to sparse_attn_2src on the decoded bf16 rows."""
+    B, T, H, D = q.shape
+    R = fp4_record_bytes(D)
+    if kv_win.dtype != torch.bfloat16 or not kv_win.is_contiguous() or kv_win.dim() != 3 \
+            or kv_win.shape[0] != B or kv_win.shape[2] != D or kv_win.device != q.device:
+        raise ValueError("kv_win must be a contiguous bf16 [B, rows, D] tensor on q's device")
+    if cmp_records.dtype != torch.uint8 or not cmp_records.is_contiguous() \
+            or cmp_records.dim() != 3 or cmp_records.shape[0] != B or cmp_records.shape[2] != R \
+            or cmp_records.device != q.device:
+        raise ValueError(f"cmp_records must be a contiguous uint8 [B, rows, {R}] tensor on q's device")
+    _check_tensors(q, kv_win, sink, idxs)
+    dims = SaDims(B, T, H, D, N, idxs.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    L = _lib.lib()
+    with torch.cuda.device(q.device):
+        need = int(L.sparse_attn_workspace_bytes(ctypes.byref(dims), num_splits))
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = L.sparse_attn_fwd_2src_fp4(_ptr(q), _ptr(kv_win), kv_win.shape[1], _ptr(cmp_records),
+                                        cmp_records.shape[1], W, _ptr(sink), _ptr(idxs),
+                                        ctypes.c_float(scale), _ptr(out), ctypes.byref(dims),
+                                        num_splits, _ptr(workspace), ws_bytes, _stream(q.device))
+    _lib.check(rc, "sparse_attn_fwd_2src_fp4")
+    return out
+
+
 def sparse_attn_partial(q, kv, idxs, scale: float, num_splits: int, workspace):
     """First kernel of the split path: per-split partials into ``workspace``."""
     _check_tensors(q, kv, None, idxs)

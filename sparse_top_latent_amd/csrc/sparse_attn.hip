@@ -58,6 +58,8 @@ struct FwdParams {
     const uint16_t *kv;     // first source  [B, rows_a, D]
     const uint16_t *kv2;    // second source [B, rows_b, D]
     int64_t W, rows_a, rows_b;
+    int32_t rec2;           // 0: the second source holds bf16 rows; else it holds FP4
+                            // records of rec2 bytes (see expand_fp4)
     const float *sink;
     const int32_t *idxs;
     uint16_t *out;     // non-split path
@@ -310,6 +312,81 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
     }
 }
 
+// OCP E4M3 (the scale format of the pages' compressed cache): sign, 4-bit
+// exponent with bias 7, 3-bit mantissa; exponent 0 is subnormal (m * 2^-9);
+// the all-ones code is NaN.  Exact in float32.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * (1.f / 512.f);
+    if (e == 15u && m == 7u) mag = __uint_as_float(0x7FC00000u);
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// f2: rows of the second source packed as the pages' cache quantises them
+// (DeepSeek-V4.1 pages, "blocks, re-index groups" page, compressor excerpt:
+// groups of 16 elements, E2M1 codes with one E4M3 scale per group).  A record
+// holds D/2 bytes of codes (byte k: element 2k in the low nibble, 2k + 1 in
+// the high one) and then D/16 scale bytes, padded to `rec` bytes.  Each
+// record lands by LDS-DMA in the last `rec` bytes of its padded ring row (RS
+// bytes); this pass rewrites those rows in place as bf16 (element i =
+// E2M1(code i) * E4M3(scale i/16), exact in bf16: 2 and 4 significant bits).
+// All codes are read before any row is written, since the bf16 row covers
+// the record.  Rows whose list entry is below W hold bf16 already.
+template <int D, int NT, int KCH>
+__device__ void expand_fp4(LDS_AS uint8_t *T, int RS, int rec, const int32_t *list, int e0, int hi,
+                           int64_t W) {
+    constexpr int G = D / 16;  // groups (and scale bytes) per row
+    constexpr int ITEMS = KCH * G;
+    constexpr int PER = (ITEMS + NT - 1) / NT;
+    const int tid = threadIdx.x;
+    const int off = RS - rec;
+    u32x2_t codes[PER];
+    uint32_t sc[PER];
+    bool on[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = k * NT + tid;
+        const int r = i / G, g = i % G;
+        const int e = e0 + r;
+        on[k] = i < ITEMS && list[e < hi ? e : e0] >= W;
+        codes[k] = u32x2_t{0u, 0u};
+        sc[k] = 0u;
+        if (on[k]) {
+            const LDS_AS uint8_t *src = T + r * RS + off;
+            codes[k] = *(const LDS_AS u32x2_t *)(src + 8 * g);
+            sc[k] = src[D / 2 + g];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if (on[k]) {
+            const int i = k * NT + tid;
+            const int r = i / G, g = i % G;
+            const float s = e4m3_to_f32(sc[k]);
+            // byte j of the group holds elements 2j, 2j + 1.  Scale 1: exact
+            // E2M1 values (the instruction applies only the power of two of its
+            // scale, so the E4M3 scale is a separate multiply).
+            const uint32_t c0 = codes[k][0], c1 = codes[k][1];
+            const f32x2_t f[8] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 0),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 1),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 2),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 3),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, 1.0f, 0),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, 1.0f, 1),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, 1.0f, 2),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, 1.0f, 3)};
+            uint32_t w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = pack2_bf16(f[j][0] * s, f[j][1] * s);
+            LDS_AS uint8_t *dst = T + r * RS + 32 * g;
+            *(LDS_AS u32x4_t *)dst = u32x4_t{w[0], w[1], w[2], w[3]};
+            *(LDS_AS u32x4_t *)(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+        }
+    }
+    __syncthreads();
+}
+
 // Work split: a workgroup holds NHQ groups of 16*HT heads; each group is
 // served by a pair of waves, one per half of the head dimension.  For QK^T a
 // wave sums over its half of d and the pair adds the two partial scores
@@ -364,9 +441,11 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 
     // head of this lane in head tile t: hw0 + 16 t + li
     const int hw0 = hg * HWG + hq * HW;
-    // row j of this sequence lives at (j < W ? kva : kvb2) + j * D
+    // row j of this sequence lives at (j < W ? kva : kvb2) + j * D, or is the
+    // FP4 record at recb + j * rec2
     const uint16_t *kva = p.kv + (int64_t)b * p.rows_a * D;
     const uint16_t *kvb2 = p.kv2 + ((int64_t)b * p.rows_b - p.W) * D;
+    const uint8_t *recb = (const uint8_t *)p.kv2 + ((int64_t)b * p.rows_b - p.W) * p.rec2;
     static_assert(NBUF == 4, "the prologue stages q in ring slots 1-2 and the list in slot 3");
 
     // Prologue.  The index list and q come in through LDS-DMA too, so every
@@ -436,9 +515,16 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
             const int r = k * NW + wid;
-            if (CPR == 64 || lane < CPR)
-                lds_dma16((row[k] < p.W ? kva : kvb2) + (int64_t)row[k] * D + lane * 8,
-                          (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS));
+            // the row number is wave-uniform: a scalar branch, one DMA either way
+            const int rw = __builtin_amdgcn_readfirstlane(row[k]);
+            if (rw < p.W || p.rec2 == 0) {
+                if (CPR == 64 || lane < CPR)
+                    lds_dma16((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8,
+                              (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS));
+            } else if (lane * 16 < p.rec2) {
+                lds_dma16(recb + (int64_t)rw * p.rec2 + lane * 16,
+                          (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS + RS - p.rec2));
+            }
         }
     };
     if (nchunks > 0) stage(0);
@@ -488,6 +574,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NBUF][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
+        if (p.rec2 > 0) expand_fp4<D, NT, KC>((LDS_AS uint8_t *)T, RS, p.rec2, list, lo + c * KC, hi, p.W);
 
         // a4: partial S^T[j, h] over this wave's half of d (two 16-row tiles
         // x HT head tiles; each K operand feeds HT MFMAs).
@@ -646,6 +733,7 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     const int hown = hg * (NHQ * HP) + hq * HP + 16 * w + li;  // head of this lane's scores
     const uint16_t *kva = p.kv + (int64_t)b * p.rows_a * D;          // rows j < W
     const uint16_t *kvb2 = p.kv2 + ((int64_t)b * p.rows_b - p.W) * D;  // rows j >= W
+    const uint8_t *recb = (const uint8_t *)p.kv2 + ((int64_t)b * p.rows_b - p.W) * p.rec2;
 
     // Prologue: the raw list into `list` by LDS-DMA.
     {
@@ -678,8 +766,13 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     auto stage_one = [&](int c, int rows, int k) {  // this wave's k-th row of chunk c
         LDS_AS uint8_t *buf = (LDS_AS uint8_t *)&tile[c % NB][0];
         const int row = __builtin_amdgcn_readlane(rows, k);
-        const uint16_t *src = (row < p.W ? kva : kvb2) + (int64_t)row * D;
-        if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, buf + (k * NW + wid) * RS);
+        if (row < p.W || p.rec2 == 0) {
+            const uint16_t *src = (row < p.W ? kva : kvb2) + (int64_t)row * D;
+            if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, buf + (k * NW + wid) * RS);
+        } else if (lane * 16 < p.rec2) {
+            lds_dma16_s(recb + (int64_t)row * p.rec2, lane * 16,
+                        buf + (k * NW + wid) * RS + RS - p.rec2);
+        }
     };
     auto stage = [&](int c, int rows) {
 #pragma unroll
@@ -723,6 +816,7 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NB][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
+        if (p.rec2 > 0) expand_fp4<D, NT, KC>((LDS_AS uint8_t *)T, RS, p.rec2, list, lo + c * KC, hi, p.W);
 
         // a4: S^T[j, hown] over the whole of d, rows j = 16 jt + 4 g + i.
         // Software-pipelined by hand: operand load i + QKP is issued right
@@ -1216,10 +1310,16 @@ int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int3
     return SA_OK;
 }
 
-int sparse_attn_fwd_2src(const void *q, const void *kv_win, int32_t win_rows, const void *kv_cmp,
-                         int32_t cmp_rows, int32_t W, const float *sink, const int32_t *idxs,
-                         float scale, void *out, const sa_dims *d, int32_t num_splits,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// shared by the two-source entry points; rec = 0 for bf16 compressed rows
+int fwd_two_source(const void *q, const void *kv_win, int32_t win_rows, const void *kv_cmp,
+                   int32_t cmp_rows, int32_t W, int32_t rec, const float *sink,
+                   const int32_t *idxs, float scale, void *out, const sa_dims *d,
+                   int32_t num_splits, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
     int rc = check_dims(d);
     if (rc != SA_OK) return rc;
     if (W < 0 || W > d->N || win_rows < W || cmp_rows < d->N - W) return SA_ERR_SHAPE;
@@ -1240,10 +1340,41 @@ int sparse_attn_fwd_2src(const void *q, const void *kv_win, int32_t win_rows, co
     p.W = W;
     p.rows_a = win_rows;
     p.rows_b = cmp_rows;
+    p.rec2 = rec;
     if (run_fwd(p, d->D, d->H, stream) != hipSuccess) return SA_ERR_HIP;
     if (S > 1 && launch_combine(d, S, sink, out, workspace, ws_layout(d, S), stream) != hipSuccess)
         return SA_ERR_HIP;
     return SA_OK;
+}
+
+// bytes of one FP4 record: D/2 code bytes + D/16 scale bytes, padded to 16
+int32_t fp4_record_bytes(int32_t D) { return (9 * D / 16 + 15) / 16 * 16; }
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_fwd_2src(const void *q, const void *kv_win, int32_t win_rows, const void *kv_cmp,
+                         int32_t cmp_rows, int32_t W, const float *sink, const int32_t *idxs,
+                         float scale, void *out, const sa_dims *d, int32_t num_splits,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return fwd_two_source(q, kv_win, win_rows, kv_cmp, cmp_rows, W, 0, sink, idxs, scale, out, d,
+                          num_splits, workspace, workspace_bytes, stream);
+}
+
+int32_t sparse_attn_fp4_record_bytes(int32_t D) {
+    return D == 128 || D == 256 || D == 512 ? fp4_record_bytes(D) : 0;
+}
+
+int sparse_attn_fwd_2src_fp4(const void *q, const void *kv_win, int32_t win_rows,
+                             const void *cmp_records, int32_t cmp_rows, int32_t W,
+                             const float *sink, const int32_t *idxs, float scale, void *out,
+                             const sa_dims *d, int32_t num_splits, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    if (d == nullptr) return SA_ERR_NULL;
+    return fwd_two_source(q, kv_win, win_rows, cmp_records, cmp_rows, W,
+                          sparse_attn_fp4_record_bytes(d->D), sink, idxs, scale, out, d,
+                          num_splits, workspace, workspace_bytes, stream);
 }
 
 int sparse_attn_fwd_partial(const void *q, const void *kv, const int32_t *idxs, float scale,

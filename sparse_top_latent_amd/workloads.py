@@ -266,3 +266,17 @@ def make_random(seed: int, B: int, T: int, H: int, D: int, N: int, K: int,
     idxs[rng.random((B, T, K)) < p_unused] = -1
     sc = D ** -0.5 if scale is None else scale
     return _finish(f"random{seed}", B, T, H, D, N, K, sc, seed, idxs)
+
+
+def make_fp4_records(seed: int, B: int, rows: int, D: int, R: int) -> np.ndarray:
+    """Synthetic packed FP4 rows (uint8 [B, rows, R]): uniform E2M1 codes in the
+    first D/2 bytes, then D/16 positive E4M3 scales with exponent field 4..5
+    (2^-3 .. 2^-2 times 1 + m/8, around the amax/6 a group of 16 N(0,1) values
+    gets), then zero padding.  Element RMS is about 1.  Tensor id 4 of the seed."""
+    rng = _rng(seed, 4)
+    rec = np.zeros((B, rows, R), dtype=np.uint8)
+    rec[..., :D // 2] = rng.integers(0, 256, (B, rows, D // 2), dtype=np.uint8)
+    exp = rng.integers(4, 6, (B, rows, D // 16))
+    man = rng.integers(0, 8, (B, rows, D // 16))
+    rec[..., D // 2:D // 2 + D // 16] = (exp << 3 | man).astype(np.uint8)
+    return rec

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     assert set(names) == set(_lib.SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -161,3 +161,20 @@ def test_two_source_argument_errors(L):
     assert fwd2(L, d=dims(D=100)) == SA_ERR_UNSUPPORTED
     # a NULL buffer that no entry can address is fine; zero queries is a no-op
     assert fwd2(L, q=None, win=None, cmp=None, d=dims(B=0), W=0) == SA_OK
+
+
+def test_fp4_record_bytes_and_errors(L):
+    assert L.sparse_attn_fp4_record_bytes(512) == 288
+    assert L.sparse_attn_fp4_record_bytes(256) == 144
+    assert L.sparse_attn_fp4_record_bytes(128) == 80     # 72 rounded up to 16
+    assert L.sparse_attn_fp4_record_bytes(100) == 0
+    f = lambda **kw: L.sparse_attn_fwd_2src_fp4(
+        kw.get("q", A), A, 100, kw.get("rec", A), kw.get("rows", 100), kw.get("W", 40), None, A,
+        ctypes.c_float(0.1), A2, kw.get("d", dims()), 1, None, 0, None)
+    assert L.sparse_attn_fwd_2src_fp4(A, A, 100, A, 100, 40, None, A, ctypes.c_float(0.1), A2,
+                                      None, 1, None, 0, None) == SA_ERR_NULL
+    assert f(W=101) == SA_ERR_SHAPE
+    assert f(rows=59) == SA_ERR_SHAPE
+    assert f(rec=None) == SA_ERR_NULL
+    assert f(rec=ctypes.c_void_p(0x10008)) == SA_ERR_ALIGN
+    assert f(d=dims(D=100)) == SA_ERR_UNSUPPORTED

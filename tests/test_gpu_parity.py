@@ -326,6 +326,82 @@ def test_two_source_full_decode():
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
 
 
+# ------------------------------------------------- FP4 compressed rows (E2M1 + E4M3 group scales)
+
+def fp4_records_for(w, W, spare=2):
+    """Packed FP4 records for the compressed rows [W, N) of workload w (plus
+    spare rows); rows no list references get NaN scale codes, so a stray read
+    shows in the output."""
+    from sparse_top_latent_amd import api
+    R = api.fp4_record_bytes(w.D)
+    rec = wl.make_fp4_records(w.seed, w.B, w.N - W + spare, w.D, R)
+    D16 = w.D // 16
+    for b in range(w.B):
+        used = np.unique(w.idxs[b][w.idxs[b] >= W]) - W
+        poison = np.ones(rec.shape[1], bool)
+        poison[used] = False
+        rec[b, poison, w.D // 2:w.D // 2 + D16] = 0x7F
+    return rec
+
+
+def check_fp4(w, W, S, what):
+    torch = torch_mod()
+    import oracle
+    from sparse_top_latent_amd import api
+    oracle.build(force=False)
+    q, kv, sk, idx = to_dev(w)
+    win_h, _, win, _ = split_sources(w, W)
+    rec_h = fp4_records_for(w, W)
+    rec = torch.from_numpy(rec_h).cuda()
+    got_t = api.sparse_attn_2src_fp4(q, win, rec, W, w.N, sk, idx, w.scale, num_splits=S)
+    # the same rows decoded (by the oracle's decoder) and given as bf16
+    cmp_bits = oracle._f64_to_bf16_bits_exact(oracle.fp4_records_to_rows(rec_h, w.D))
+    cmp_t = torch.from_numpy(cmp_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    bf = api.sparse_attn_2src(q, win, cmp_t, W, w.N, sk, idx, w.scale, num_splits=S)
+    torch.cuda.synchronize()
+    assert torch.equal(got_t.view(torch.int16), bf.view(torch.int16)), f"{what}: differs from bf16 rows"
+    got = wl.bf16_bits_to_f32(got_t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    exp = oracle.sparse_attn_2src_fp4_ref(w.q, win_h, rec_h, W, w.N, w.sink, w.idxs, w.scale)
+    assert_close(got, exp, what)
+
+
+@pytest.mark.parametrize("W,S", [(128, 1), (128, 3), (0, 2), (300, 1)])
+def test_fp4_compressed_rows(W, S):
+    w = wl.make_random(230, 2, 3, 64, 512, 300, 173, p_unused=0.3)
+    check_fp4(w, W, S, f"fp4 W={W} S={S}")
+
+
+@pytest.mark.parametrize("H,D", [(16, 128), (32, 256)])
+def test_fp4_other_head_dims(H, D):
+    w = wl.make_random(231 + D, 2, 2, H, D, 200, 90, p_unused=0.2)
+    check_fp4(w, 64, 1, f"fp4 H={H} D={D}")
+
+
+def test_fp4_many_query_path():
+    w = wl.make_random(233, 2, many_query_T(), 64, 512, 160, 75, p_unused=0.3)
+    check_fp4(w, 40, 0, "fp4 many-query")
+
+
+def test_fp4_full_decode():
+    # decode shape: 128-row bf16 window ring + FP4 compressed cache; every query
+    # bit for bit the bf16 two-source result on the decoded rows
+    torch = torch_mod()
+    import oracle
+    from sparse_top_latent_amd import api
+    w = wl.make("decode")
+    q, kv, sk, idx = to_dev(w)
+    win = kv[:, :128].contiguous()
+    R = api.fp4_record_bytes(w.D)
+    rec_h = wl.make_fp4_records(w.seed, w.B, w.N - 128, w.D, R)
+    rec = torch.from_numpy(rec_h).cuda()
+    cmp_bits = oracle._f64_to_bf16_bits_exact(oracle.fp4_records_to_rows(rec_h, w.D))
+    cmp_t = torch.from_numpy(cmp_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    a = api.sparse_attn_2src_fp4(q, win, rec, 128, w.N, sk, idx, w.scale)
+    b = api.sparse_attn_2src(q, win, cmp_t, 128, w.N, sk, idx, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 # --------------------------------------------------------- full-size workloads
 # Same launch configuration as bench.py: num_splits=0 (planned by the library).
 

@@ -87,3 +87,32 @@ def test_two_source_oracle_pinned():
     zero = oracle.sparse_attn_ref(q, cmp_[:, :C], sink, np.where(idxs < C, idxs, -1), 0.3)
     assert np.array_equal(oracle.sparse_attn_2src_ref(q, win, cmp_, 0, C, sink,
                                                       np.where(idxs < C, idxs, -1), 0.3), zero)
+
+
+
+def test_fp4_decoders_pinned():
+    """E2M1 against the format's value table, E4M3 against torch's float8_e4m3fn
+    for all 256 codes, the record layout on a hand-built record, and exactness
+    of every product in bf16."""
+    import torch
+    import oracle
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert oracle.e2m1_values(np.arange(8)).tolist() == table
+    assert oracle.e2m1_values(np.arange(8, 16)).tolist() == [-v for v in table]
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_values(np.arange(256))
+    assert np.array_equal(got, ref, equal_nan=True)
+    # a record for D=32: codes of elements 0..31, two scales (1.0 and 0.375)
+    D = 32
+    rec = np.zeros(32, np.uint8)                      # 16 code bytes + 2 scales + padding
+    codes = np.arange(32) % 16
+    rec[:16] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    rec[16] = 0x38                                     # 1.0
+    rec[17] = 0x2C                                     # 2^-2 * 1.5 = 0.375
+    row = oracle.fp4_records_to_rows(rec[None], D)[0]
+    exp = np.array([(table[c & 7] * (-1 if c & 8 else 1)) for c in codes])
+    exp[16:] *= 0.375
+    assert np.array_equal(row, exp)
+    # every code times every finite scale is exact in bf16
+    allv = np.outer(oracle.e2m1_values(np.arange(16)), got[np.isfinite(got)])
+    oracle._f64_to_bf16_bits_exact(allv)
