@@ -154,8 +154,10 @@ int sparse_attn_check_idxs(const int32_t *idxs, const sa_dims *d, int32_t *d_bad
  * planned) launches on the current device, as profilers list it (static
  * text), or NULL on bad arguments or a failed device query.  Launches of at
  * least two workgroups per compute unit take the many-query kernel (two
- * workgroups share a unit); smaller ones the deep-gather kernel.  For
- * profiling and reports; no call needs it. */
+ * workgroups share a unit); smaller ones the deep-gather kernel.  The name is
+ * that of the bf16-rows build (sparse_attn_fwd_2src_fp4 runs the same kernel
+ * built with FP4 records, <..., true>).  For profiling and reports; no call
+ * needs it. */
 const char *sparse_attn_plan_kernel(const sa_dims *d, int32_t num_splits);
 
 /* Static text for a status code (never NULL). */

@@ -395,7 +395,7 @@ __device__ void expand_fp4(LDS_AS uint8_t *T, int RS, int rec, const int32_t *li
 // holds HT tiles of 16 heads: every K or V operand it reads from LDS feeds HT
 // MFMAs, so LDS read traffic per chunk falls as 1/HT, at the cost of HT x
 // (16 x D/2) accumulators and query values in registers.
-template <int D, int NHQ, int HT>
+template <int D, int NHQ, int HT, bool FP4>
 __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     constexpr int NW = 2 * NHQ;            // waves per workgroup
     constexpr int NT = NW * 64;
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             const int r = k * NW + wid;
             // the row number is wave-uniform: a scalar branch, one DMA either way
             const int rw = __builtin_amdgcn_readfirstlane(row[k]);
-            if (rw < p.W || p.rec2 == 0) {
+            if (!FP4 || rw < p.W) {
                 if (CPR == 64 || lane < CPR)
                     lds_dma16((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8,
                               (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS));
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NBUF][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
-        if (p.rec2 > 0) expand_fp4<D, NT, KC>((LDS_AS uint8_t *)T, RS, p.rec2, list, lo + c * KC, hi, p.W);
+        if (FP4) expand_fp4<D, NT, KC>((LDS_AS uint8_t *)T, RS, p.rec2, list, lo + c * KC, hi, p.W);
 
         // a4: partial S^T[j, h] over this wave's half of d (two 16-row tiles
         // x HT head tiles; each K operand feeds HT MFMAs).
@@ -696,7 +696,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 //     (compacted in place, sized by K in dynamic LDS) take about 75 KB of
 //     LDS, so two workgroups share a compute unit and one's softmax,
 //     barriers, prologue and epilogue overlap the other's MFMAs.
-template <int D, int NHQ>
+template <int D, int NHQ, bool FP4>
 __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) {
     constexpr int HT = 2;                  // head tiles per pair
     constexpr int NW = 2 * NHQ;            // waves per workgroup
@@ -763,15 +763,16 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         const int e = e0 + (lane % IPW) * NW + wid;
         return list[e < hi ? e : e0];
     };
-    auto stage_one = [&](int c, int rows, int k) {  // this wave's k-th row of chunk c
-        LDS_AS uint8_t *buf = (LDS_AS uint8_t *)&tile[c % NB][0];
+    // this wave's k-th row of chunk c: a bf16 row, or (FP4 build, rows >= W)
+    // a record landing at the tail of the row's slot
+    auto stage_one = [&](int c, int rows, int k) {
         const int row = __builtin_amdgcn_readlane(rows, k);
-        if (row < p.W || p.rec2 == 0) {
+        LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NB][0] + (k * NW + wid) * RS;
+        if (!FP4 || row < p.W) {
             const uint16_t *src = (row < p.W ? kva : kvb2) + (int64_t)row * D;
-            if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, buf + (k * NW + wid) * RS);
+            if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, dst);
         } else if (lane * 16 < p.rec2) {
-            lds_dma16_s(recb + (int64_t)row * p.rec2, lane * 16,
-                        buf + (k * NW + wid) * RS + RS - p.rec2);
+            lds_dma16_s(recb + (int64_t)row * p.rec2, lane * 16, dst + RS - p.rec2);
         }
     };
     auto stage = [&](int c, int rows) {
@@ -816,7 +817,7 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NB][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
-        if (p.rec2 > 0) expand_fp4<D, NT, KC>((LDS_AS uint8_t *)T, RS, p.rec2, list, lo + c * KC, hi, p.W);
+        if (FP4) expand_fp4<D, NT, KC>((LDS_AS uint8_t *)T, RS, p.rec2, list, lo + c * KC, hi, p.W);
 
         // a4: S^T[j, hown] over the whole of d, rows j = 16 jt + 4 g + i.
         // Software-pipelined by hand: operand load i + QKP is issued right
@@ -1135,14 +1136,19 @@ int plan_splits(const sa_dims *d) {
 template <int D, int NHQ, int HT>
 hipError_t launch_fwd(const FwdParams &p, hipStream_t stream) {
     const int grid = 8 * p.per_xcd;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ, HT>), dim3(grid), dim3(NHQ * 128), 0, stream, p);
+    // bf16 rows only, or FP4 records in the second source (a separate build of
+    // the kernel, so the bf16 one carries none of the expansion code)
+    if (p.rec2 > 0)
+        hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ, HT, true>), dim3(grid), dim3(NHQ * 128), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ, HT, false>), dim3(grid), dim3(NHQ * 128), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_fwd_d(WgShape w, const FwdParams &p, hipStream_t stream) {
     if (w.ht == 1) return w.nhq == 4 ? launch_fwd<D, 4, 1>(p, stream) : launch_fwd<D, 1, 1>(p, stream);
-    return w.nhq == 2 ? launch_fwd<D, 2, 2>(p, stream) : launch_fwd<D, 1, 2>(p, stream);
+    return launch_fwd<D, 1, 2>(p, stream);
 }
 
 hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
@@ -1237,8 +1243,12 @@ template <int D, int NHQ>
 hipError_t launch_mq(const FwdParams &p, hipStream_t stream) {
     const int grid = 8 * p.per_xcd;
     const size_t list_bytes = ((size_t)(p.K > 0 ? p.K : 1) * 4 + 15) / 16 * 16;
-    hipLaunchKernelGGL((attn_fwd_mq_kernel<D, NHQ>), dim3(grid), dim3(NHQ * 128), list_bytes,
-                       stream, p);
+    if (p.rec2 > 0)
+        hipLaunchKernelGGL((attn_fwd_mq_kernel<D, NHQ, true>), dim3(grid), dim3(NHQ * 128),
+                           list_bytes, stream, p);
+    else
+        hipLaunchKernelGGL((attn_fwd_mq_kernel<D, NHQ, false>), dim3(grid), dim3(NHQ * 128),
+                           list_bytes, stream, p);
     return hipGetLastError();
 }
 
@@ -1432,16 +1442,16 @@ const char *sparse_attn_plan_kernel(const sa_dims *d, int32_t num_splits) {
     if (use_mq(p, d->H)) {
         const bool two = d->H > 32;
         switch (d->D) {
-            case 128: return two ? "attn_fwd_mq_kernel<128,2>" : "attn_fwd_mq_kernel<128,1>";
-            case 256: return two ? "attn_fwd_mq_kernel<256,2>" : "attn_fwd_mq_kernel<256,1>";
-            default: return two ? "attn_fwd_mq_kernel<512,2>" : "attn_fwd_mq_kernel<512,1>";
+            case 128: return two ? "attn_fwd_mq_kernel<128,2,false>" : "attn_fwd_mq_kernel<128,1,false>";
+            case 256: return two ? "attn_fwd_mq_kernel<256,2,false>" : "attn_fwd_mq_kernel<256,1,false>";
+            default: return two ? "attn_fwd_mq_kernel<512,2,false>" : "attn_fwd_mq_kernel<512,1,false>";
         }
     }
     const WgShape w = shape_for(d->H);
     static const char *names[3][3] = {
-        {"attn_fwd_kernel<128,4,1>", "attn_fwd_kernel<128,1,2>", "attn_fwd_kernel<128,1,1>"},
-        {"attn_fwd_kernel<256,4,1>", "attn_fwd_kernel<256,1,2>", "attn_fwd_kernel<256,1,1>"},
-        {"attn_fwd_kernel<512,4,1>", "attn_fwd_kernel<512,1,2>", "attn_fwd_kernel<512,1,1>"}};
+        {"attn_fwd_kernel<128,4,1,false>", "attn_fwd_kernel<128,1,2,false>", "attn_fwd_kernel<128,1,1,false>"},
+        {"attn_fwd_kernel<256,4,1,false>", "attn_fwd_kernel<256,1,2,false>", "attn_fwd_kernel<256,1,1,false>"},
+        {"attn_fwd_kernel<512,4,1,false>", "attn_fwd_kernel<512,1,2,false>", "attn_fwd_kernel<512,1,1,false>"}};
     const int di = d->D == 128 ? 0 : d->D == 256 ? 1 : 2;
     const int wi = w.ht == 1 ? (w.nhq == 4 ? 0 : 2) : 1;
     return names[di][wi];

@@ -238,10 +238,10 @@ def test_plan_kernel_names_the_dispatch():
     from sparse_top_latent_amd import api
     w = wl.make_decode(B=4)
     q, kv, _, idx = to_dev(w)
-    assert api.plan_kernel(q, kv, idx, 4) == "attn_fwd_kernel<512,4,1>"
+    assert api.plan_kernel(q, kv, idx, 4) == "attn_fwd_kernel<512,4,1,false>"
     wm = wl.make_random(212, 2, many_query_T(), 64, 512, 60, 20)
     q, kv, _, idx = to_dev(wm)
-    assert api.plan_kernel(q, kv, idx, 0) == "attn_fwd_mq_kernel<512,2>"
+    assert api.plan_kernel(q, kv, idx, 0) == "attn_fwd_mq_kernel<512,2,false>"
 
 
 def test_many_query_splits_stress_and_long_lists(ref):
