@@ -142,6 +142,30 @@ def sparse_attn_2src_fp4_ref(q_bits, win_bits, records, W, N, sink, idxs, scale)
                                 idxs, scale)
 
 
+def topk_ref(scores, lens, k, offset):
+    """The compressed segment of the index lists from indexer scores
+    (DeepSeek-V4.1 pages, "blocks, re-index groups" page, _compress_topk_idxs
+    excerpt: the top index_topk compressed positions per query, offset by the
+    window length, -1 where fewer are visible).  Query q sees positions
+    0 .. lens[q]-1 (all when lens is None); the min(k, visible) best scores are
+    taken, NaN ranked below every number, -0 equal to +0, equal scores by
+    ascending position; the positions + offset are listed in ascending order,
+    then -1 up to k.  Returns int32 [Q, k]."""
+    sc = np.asarray(scores, dtype=np.float64)
+    Q, C = sc.shape
+    out = np.full((Q, k), -1, dtype=np.int32)
+    for qi in range(Q):
+        L = C if lens is None else int(min(max(lens[qi], 0), C))
+        row = sc[qi, :L]
+        nan = np.isnan(row)
+        # primary key: -value (NaN last), secondary: position
+        primary = np.where(nan, np.inf, -np.where(row == 0, 0.0, row))
+        order = np.lexsort((np.arange(L), nan.astype(np.int8), primary))
+        take = np.sort(order[:min(k, L)])
+        out[qi, :len(take)] = take + offset
+    return out
+
+
 def ref_from_library(path):
     """The same interface over another build of the oracle's C entry point
     (the tests use it to run the pins against planted mistakes)."""

@@ -116,3 +116,41 @@ def test_fp4_decoders_pinned():
     # every code times every finite scale is exact in bf16
     allv = np.outer(oracle.e2m1_values(np.arange(16)), got[np.isfinite(got)])
     oracle._f64_to_bf16_bits_exact(allv)
+
+
+
+def brute_topk(row, k, offset):
+    """Top-k written from the ranking rule with Python's sorted(): NaN lowest,
+    -0 = +0, ties by position; positions listed ascending."""
+    def rank(i):
+        v = float(row[i])
+        return (1, 0.0, i) if v != v else (0, -(v + 0.0), i)
+    best = sorted(range(len(row)), key=rank)[:k]
+    return sorted(j + offset for j in best)
+
+
+def test_topk_oracle_pinned():
+    import oracle
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        C = int(rng.integers(0, 40))
+        k = int(rng.integers(0, 45))
+        row = rng.integers(-3, 4, C).astype(np.float64)          # many ties
+        if C:
+            row[rng.random(C) < 0.1] = np.nan
+            row[rng.random(C) < 0.1] = -0.0
+            row[rng.random(C) < 0.05] = np.inf
+            row[rng.random(C) < 0.05] = -np.inf
+        L = int(rng.integers(0, C + 3))
+        got = oracle.topk_ref(row[None], None if trial % 2 else [L], k, 7)[0]
+        vis = row if trial % 2 else row[:min(L, C)]
+        exp = brute_topk(vis, k, 7)
+        assert got[:len(exp)].tolist() == exp and np.all(got[len(exp):] == -1)
+        # property: every taken score >= every visible score not taken
+        taken = set(exp)
+        tv = [vis[j - 7] for j in exp]
+        rest = [vis[i] for i in range(len(vis)) if i + 7 not in taken]
+        if tv and rest:
+            lo = min((v for v in tv if v == v), default=None)
+            hi = max((v for v in rest if v == v), default=None)
+            assert lo is None or hi is None or lo >= hi
