@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--kv-format", default="bf16", choices=["bf16", "fp4"],
                     help="fp4: also time the step with the compressed rows packed as FP4 "
                          "records (E2M1 codes, one E4M3 scale per 16) beside bf16 window rows")
+    ap.add_argument("--topk", action="store_true",
+                    help="also time the top-k selection that fills the lists' compressed "
+                         "segment (decode and causal prefill shapes) and decode top-k + attention")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run plain 256 MiB copies first (HBM counter calibration)")
     return ap.parse_args()
@@ -236,6 +239,26 @@ def main():
         "roofline": roof,
     }
 
+    def time_graph(fn):
+        """ms per call of fn(i), replayed from a graph of R calls (one per copy)."""
+        for i in range(R):
+            fn(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for i in range(R):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        gate(torch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.steps // R)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * R)
+
     if args.two_source:
         # the rows as the model holds them: window rows and compressed rows in
         # separate buffers; the one-buffer path needs them concatenated first
@@ -249,25 +272,6 @@ def main():
 
         def cat(i):
             torch.cat([wins[i], cmps[i]], dim=1)
-
-        def time_graph(fn):
-            for i in range(R):
-                fn(i)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap_stream):
-                for i in range(R):
-                    fn(i)
-            g.replay()
-            torch.cuda.synchronize()
-            gate(torch)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = max(1, args.steps // R)
-            e0.record()
-            for _ in range(reps):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / (reps * R)
 
         ms2 = time_graph(step2)
         ms_cat = time_graph(cat)
@@ -290,23 +294,7 @@ def main():
             api.sparse_attn_2src_fp4(qs[i], wins4[i], recs[i], W, w.N, sink, idxs[i], w.scale,
                                      out=out, num_splits=S, workspace=ws)
 
-        for i in range(R):
-            step4(i)
-        g4 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g4, stream=cap_stream):
-            for i in range(R):
-                step4(i)
-        g4.replay()
-        torch.cuda.synchronize()
-        gate(torch)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(1, args.steps // R)
-        e0.record()
-        for _ in range(reps):
-            g4.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms4 = e0.elapsed_time(e1) / (reps * R)
+        ms4 = time_graph(step4)
         # algorithmic bytes: distinct window rows x 2D + distinct compressed rows x record
         nwin = sum(int(np.count_nonzero(np.asarray(r) < W)) for r in w.rows)
         ncmp = sum(int(np.count_nonzero(np.asarray(r) >= W)) for r in w.rows)
@@ -318,6 +306,42 @@ def main():
             "path_roofline_frac": round(t4 / (ms4 * 1e-3), 4),
             "note": "window rows bf16; compressed rows as FP4 records (E2M1 codes + one E4M3 "
                     "scale per 16 elements), expanded to bf16 in LDS"}
+
+
+    if args.topk:
+        # the compressed segment of the lists from indexer scores: the decode
+        # batch (64 queries x 8192 compressed positions -> 512, written after
+        # the window entries) and the causal prefill shape (4096 queries, query
+        # t sees (t+1)//2 of 2048 positions), then decode top-k + attention
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        TOPK = 512
+        res = {}
+        for name, Qk, Ck, causal in (("decode", w.B * w.T, 8192, False),
+                                      ("prefill", 4096, 2048, True)):
+            scs = [torch.randn(Qk, Ck, generator=gen, device=dev) for _ in range(R)]
+            lens = (torch.arange(1, Qk + 1, device=dev, dtype=torch.int32) // 2) if causal else None
+            outk = torch.empty(Qk, TOPK, dtype=torch.int32, device=dev)
+            ms_k = time_graph(lambda i: api.topk(scs[i], TOPK, 128, lens=lens, out=outk))
+            nbytes = Qk * Ck * 4 + Qk * TOPK * 4 + (Qk * 4 if causal else 0)
+            res[name] = {"queries": Qk, "candidates": Ck, "k": TOPK, "ms": round(ms_k, 5),
+                         "GBps": round(nbytes / (ms_k * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(nbytes / (ms_k * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        if w.T == 1 and w.K >= 128 + TOPK:
+            scd = [torch.randn(w.B, 8192, generator=gen, device=dev) for _ in range(R)]
+            lists = [x.clone() for x in idxs]
+
+            def step_k(i):
+                api.topk(scd[i], TOPK, 128, out=lists[i][:, 0, 128:128 + TOPK])
+                api.sparse_attn(qs[i], kvs[i], sink, lists[i], w.scale, out=out, num_splits=S,
+                                workspace=ws)
+
+            # the rows picked here are random positions of kv, so the step
+            # gathers the same number of rows as the benchmark step
+            ms_kd = time_graph(step_k)
+            res["decode_with_attention"] = {"ms_per_step": round(ms_kd, 5),
+                                            "value": round(Qn / (ms_kd * 1e-3), 1)}
+        line["topk"] = res
 
     if not args.no_cpu_baseline:
         import oracle

@@ -144,6 +144,26 @@ int sparse_attn_fwd_partial(const void *q, const void *kv, const int32_t *idxs, 
 int sparse_attn_fwd_combine(const float *sink, void *out, const sa_dims *d, int32_t num_splits,
                             const void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The index lists' compressed segment from indexer scores (DeepSeek-V4.1 pages,
+ * "blocks, re-index groups" page, _compress_topk_idxs excerpt: index_topk = 512
+ * compressed positions per query, int32, offset by the window length, -1 where
+ * fewer are visible).
+ *   scores  fp32 [Q, C]: the score of compressed position c for query q
+ *   lens    int32 [Q] or NULL: query q sees positions 0 .. lens[q]-1 (clamped
+ *           to [0, C]); NULL = all C
+ *   out     int32, row q at out + q * out_stride (out_stride >= k, so a call can
+ *           write the compressed segment of [B, T, K] lists in place): the
+ *           indices + offset of the min(k, visible) best scores, in ascending
+ *           index order, then -1 up to k.
+ * Ranking: by value, NaN below every number, -0 equal to +0; equal scores are
+ * taken in ascending index order, so the result is unique.  One workgroup per
+ * query; C <= 16384 keeps the scores in registers, longer rows are re-read from
+ * memory on each radix pass.
+ * Errors: SA_ERR_SHAPE (negative sizes, out_stride < k, offset + C beyond
+ * int32), SA_ERR_NULL, SA_ERR_ALIGN (4 bytes), SA_ERR_HIP.  Only enqueues. */
+int sparse_attn_topk(const float *scores, const int32_t *lens, int32_t Q, int32_t C, int32_t k,
+                     int32_t offset, int32_t *out, int64_t out_stride, hipStream_t stream);
+
 /* Checked mode: adds to *d_bad_count (a device int32, zeroed by the caller)
  * the number of entries of idxs that are >= N.  Such entries break the
  * contract of sparse_attn_fwd (the fast path skips them). */

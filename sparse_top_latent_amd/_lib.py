@@ -21,6 +21,7 @@ SYMBOLS = (
     "sparse_attn_fwd_partial",
     "sparse_attn_fwd_combine",
     "sparse_attn_check_idxs",
+    "sparse_attn_topk",
     "sparse_attn_plan_kernel",
     "sparse_attn_status_str",
 )
@@ -66,6 +67,8 @@ def lib():
         L.sparse_attn_fwd_combine.restype = ctypes.c_int
         L.sparse_attn_check_idxs.argtypes = [P, D, P, P]
         L.sparse_attn_check_idxs.restype = ctypes.c_int
+        L.sparse_attn_topk.argtypes = [P, P, I32, I32, I32, I32, P, ctypes.c_int64, P]
+        L.sparse_attn_topk.restype = ctypes.c_int
         L.sparse_attn_plan_kernel.argtypes = [D, I32]
         L.sparse_attn_plan_kernel.restype = ctypes.c_char_p
         L.sparse_attn_status_str.argtypes = [ctypes.c_int]

@@ -12,6 +12,8 @@ from __future__ import annotations
 
 import ctypes
 
+import numpy as np
+
 import torch
 
 from . import _lib
@@ -186,6 +188,37 @@ def sparse_attn_combine(q_shape, N: int, K: int, sink, out, num_splits: int, wor
             _ptr(sink), _ptr(out), ctypes.byref(dims), num_splits, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(out.device))
     _lib.check(rc, "sparse_attn_fwd_combine")
+
+
+def topk(scores, k: int, offset: int = 0, lens=None, out=None):
+    """Compressed segment of the index lists: for each row of scores (fp32
+    [..., C]) the positions + offset of the min(k, visible) best scores in
+    ascending order, -1 after; lens (int32 [...]) limits the visible positions.
+    ``out`` may be a strided view (e.g. lists[..., W:W + k]) whose last
+    dimension is contiguous; it is written in place."""
+    if scores.dtype != torch.float32 or not scores.is_contiguous() or not scores.is_cuda:
+        raise TypeError("scores must be a contiguous float32 CUDA tensor")
+    lead = scores.shape[:-1]
+    C = scores.shape[-1]
+    Q = int(np.prod(lead)) if len(lead) else 1
+    if lens is not None:
+        if lens.dtype != torch.int32 or not lens.is_contiguous() or lens.shape != lead \
+                or lens.device != scores.device:
+            raise TypeError("lens must be a contiguous int32 tensor shaped like scores[..., 0]")
+    if out is None:
+        out = torch.empty(*lead, k, dtype=torch.int32, device=scores.device)
+    if out.dtype != torch.int32 or out.shape != (*lead, k) or out.stride(-1) != 1:
+        raise ValueError("out must be int32 [..., k] with a contiguous last dimension")
+    # rows of out must be evenly spaced
+    stride = out.stride(-2) if out.dim() >= 2 else k
+    if out.dim() >= 2 and not all(out.stride(i) == out.stride(i + 1) * out.shape[i + 1]
+                                  for i in range(out.dim() - 2)):
+        raise ValueError("out rows must be evenly spaced")
+    with torch.cuda.device(scores.device):
+        rc = _lib.lib().sparse_attn_topk(_ptr(scores), _ptr(lens), Q, C, k, offset, _ptr(out),
+                                         stride, _stream(scores.device))
+    _lib.check(rc, "sparse_attn_topk")
+    return out
 
 
 def check_idxs(idxs, N: int) -> int:

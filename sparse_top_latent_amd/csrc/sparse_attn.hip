@@ -1051,6 +1051,288 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     }
 }
 
+// f4: top-k selection of compressed positions (DeepSeek-V4.1 pages, "blocks,
+// re-index groups" page, the _compress_topk_idxs excerpt: index_topk positions
+// per query, int32 lists offset by the window length, -1 where fewer are
+// visible).  Scores are ranked by value as an unsigned key: NaN lowest, -0 and
+// +0 equal; equal keys are taken in ascending index order.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    if (f != f) return 0u;        // NaN below everything
+    if (f == 0.f) f = 0.f;        // -0 -> +0
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts by 1, 2, 4
+// and 8 lanes (DPP, within each row of 16) scan the rows, then the totals of
+// the lower rows are added from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    const int lane = threadIdx.x & 63;
+    const int r15 = __builtin_amdgcn_readlane(x, 15);
+    const int r31 = __builtin_amdgcn_readlane(x, 31);
+    const int r47 = __builtin_amdgcn_readlane(x, 47);
+    return x + (lane >= 16 ? r15 : 0) + (lane >= 32 ? r31 : 0) + (lane >= 48 ? r47 : 0);
+}
+
+// Exclusive prefix sum over the NT threads of a workgroup; returns the sum of
+// the lower threads' values, and the total in *total.  ws holds NT/64 ints.
+template <int NT>
+__device__ int block_exclusive_scan(int v, int *ws, int *total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int incl = wave_inclusive_scan(v);
+    if (lane == 63) ws[wid] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int c = ws[w];
+        before += w < wid ? c : 0;
+        all += c;
+    }
+    __syncthreads();  // ws may be reused
+    *total = all;
+    return before + incl - v;
+}
+
+// Radix digits of the select, most significant first: 11, 11 and 10 bits
+// (2048 bins), so that one pass usually leaves a single key per bin near the
+// k-th and two passes suffice.
+constexpr int TOPK_BINS = 2048;
+__device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 1023u : 2047u; }
+
+// The digit of the current pass where the count of keys from the top reaches
+// `need`.  Thread t owns the BPT bins just below 2048 - t*BPT (so lower
+// threads hold higher digits); a workgroup scan of the chunk sums gives the
+// count above each chunk, and the thread whose chunk holds the crossing walks
+// its bins.  Leaves the digit, what is still needed within it and its bin
+// count in sh[0..2].  Every thread calls it; it ends with a barrier.
+template <int NT>
+__device__ void find_digit(const int *hist, int need, int *ws, int *sh) {
+    constexpr int BPT = TOPK_BINS / NT, NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int lo = TOPK_BINS - (tid + 1) * BPT;
+    int h[BPT], sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        h[j] = hist[lo + j];
+        sum += h[j];
+    }
+    const int incl = wave_inclusive_scan(sum);
+    if (lane == 63) ws[wid] = incl;
+    __syncthreads();
+    int above = incl - sum;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) above += w < wid ? ws[w] : 0;
+    if (above < need && above + sum >= need) {
+#pragma unroll
+        for (int j = BPT - 1; j >= 0; --j) {
+            if (above < need && above + h[j] >= need) {
+                sh[0] = lo + j;
+                sh[1] = need - above;
+                sh[2] = h[j];
+            }
+            above += h[j];
+        }
+    }
+    __syncthreads();
+}
+
+// One workgroup per query, KPT keys per thread in registers (thread t holds
+// positions t*KPT .. t*KPT+KPT-1, so the workgroup covers NT*KPT positions).
+// A radix select over the keys narrows the key of the k-th best down to a
+// prefix; it stops early once every key that matches the prefix is taken.
+// Then one scan of the packed counts (keys above the prefix, keys equal to it)
+// gives each thread its output position.  Per key the work is branch-free:
+// keys outside the prefix add to a per-lane spare counter instead of a bin,
+// and each thread writes its picks in index order into an LDS row (non-picks
+// to its spare slot), which the workgroup then copies out; k above the LDS
+// row stores the picks directly.
+constexpr int TOPK_STAGE = TOPK_BINS;  // picks staged in LDS up to this k
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_reg_kernel(const float *__restrict__ scores,
+                                                      const int32_t *__restrict__ lens, int32_t C,
+                                                      int32_t k, int32_t offset, int32_t *out,
+                                                      int64_t out_stride) {
+    static_assert(NT >= 64 && TOPK_BINS % NT == 0 && KPT % 4 == 0, "bins per thread, float4 loads");
+    // two histograms used by alternate passes, each with 64 spare counters
+    __shared__ __attribute__((aligned(16))) int hist[2][TOPK_BINS + 64];
+    __shared__ int ws[NT / 64];
+    __shared__ int sh[3];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t q = blockIdx.x;
+    const float *s = scores + q * C;
+    int L = lens != nullptr ? lens[q] : C;
+    L = L < 0 ? 0 : (L > C ? C : L);
+    const int kk = k < L ? k : L;
+    int32_t *o = out + q * out_stride;
+    for (int j = kk + tid; j < k; j += NT) o[j] = -1;
+    if (kk == L) {  // everything visible is taken
+        for (int j = tid; j < L; j += NT) o[j] = j + offset;
+        return;
+    }
+    const int base = tid * KPT;
+    const int nv = L - base < 0 ? 0 : (L - base > KPT ? KPT : L - base);
+    const bool vec = ((C & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
+    uint32_t key[KPT];
+    if (vec && nv == KPT) {
+#pragma unroll
+        for (int g = 0; g < KPT / 4; ++g) {
+            const float4 f = *reinterpret_cast<const float4 *>(s + base + 4 * g);
+            key[4 * g] = score_key(f.x), key[4 * g + 1] = score_key(f.y);
+            key[4 * g + 2] = score_key(f.z), key[4 * g + 3] = score_key(f.w);
+        }
+    } else {  // slots past the visible length get key 0, taken off bin 0 below
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = j < nv ? score_key(s[base + j]) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < TOPK_BINS / NT; ++j) hist[0][tid + j * NT] = 0;
+    __syncthreads();
+
+    // pass 0: every key counts, by its top digit
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) atomicAdd(&hist[0][key[j] >> 21], 1);
+    if (tid == 0 && NT * KPT > L) atomicAdd(&hist[0][0], L - NT * KPT);
+#pragma unroll
+    for (int j = 0; j < TOPK_BINS / NT; ++j) hist[1][tid + j * NT] = 0;
+    __syncthreads();
+    find_digit<NT>(hist[0], kk, ws, sh);
+    uint32_t prefix = (uint32_t)sh[0] << 21, mask = 2047u << 21;
+    int need = sh[1];  // still to take among the keys that match the prefix
+#pragma unroll 1
+    for (int pass = 1; pass < 3 && sh[2] != need; ++pass) {
+        const int shift = digit_shift(pass);
+        const uint32_t dm = digit_mask(pass);
+        int *hc = hist[pass & 1];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const bool in = j < nv && (key[j] & mask) == prefix;
+            atomicAdd(&hc[in ? (int)((key[j] >> shift) & dm) : TOPK_BINS + lane], 1);
+        }
+        // the other histogram was last read before the previous barrier
+        if (pass < 2) {
+#pragma unroll
+            for (int j = 0; j < TOPK_BINS / NT; ++j) hist[(pass + 1) & 1][tid + j * NT] = 0;
+        }
+        __syncthreads();
+        find_digit<NT>(hc, need, ws, sh);
+        prefix |= (uint32_t)sh[0] << shift;
+        mask |= dm << shift;
+        need = sh[1];
+    }
+    // (the loop ends once every key that matches the prefix is taken)
+    // take every key whose masked value is above the prefix and the first
+    // `need` (by index) equal to it; counts < 2^16 pack into one scan
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const uint32_t m = key[j] & mask;
+        gt += j < nv && m > prefix;
+        eq += j < nv && m == prefix;
+    }
+    int tot;
+    const int before = block_exclusive_scan<NT>((eq << 16) | gt, ws, &tot);
+    const int eq_before = before >> 16, gt_before = before & 0xFFFF;
+    int take_eq = need - eq_before;
+    take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
+    int pos = gt_before + (eq_before < need ? eq_before : need);
+    if (kk <= TOPK_STAGE) {  // uniform
+        int *row = hist[0];  // free: the passes are over (barrier in the scan)
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t m = key[j] & mask;
+            const bool tie = j < nv && m == prefix && take_eq > 0;
+            const bool pick = (j < nv && m > prefix) || tie;
+            row[pick && pos < kk ? pos : TOPK_BINS + lane] = base + j + offset;
+            pos += pick;
+            take_eq -= tie;
+        }
+        __syncthreads();
+        for (int j = tid; j < kk; j += NT) o[j] = row[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t m = key[j] & mask;
+            if (j < nv && (m > prefix || (m == prefix && take_eq > 0))) {
+                if (m == prefix) --take_eq;
+                if (pos < kk) o[pos] = base + j + offset;
+                ++pos;
+            }
+        }
+    }
+}
+
+// Rows longer than the register kernels hold: the same selection with the
+// scores re-read from memory on every pass.  Thread t owns a contiguous
+// segment of positions for the final, order-keeping write.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_long_kernel(const float *__restrict__ scores,
+                                                       const int32_t *__restrict__ lens,
+                                                       int32_t C, int32_t k, int32_t offset,
+                                                       int32_t *out, int64_t out_stride) {
+    static_assert(TOPK_BINS % NT == 0, "bins per thread");
+    __shared__ __attribute__((aligned(16))) int hist[TOPK_BINS];
+    __shared__ int ws[NT / 64];
+    __shared__ int sh[3];
+    const int tid = threadIdx.x;
+    const int64_t q = blockIdx.x;
+    const float *s = scores + q * C;
+    int L = lens != nullptr ? lens[q] : C;
+    L = L < 0 ? 0 : (L > C ? C : L);
+    const int kk = k < L ? k : L;
+    int32_t *o = out + q * out_stride;
+    for (int j = kk + tid; j < k; j += NT) o[j] = -1;
+    if (kk == L) {
+        for (int j = tid; j < L; j += NT) o[j] = j + offset;
+        return;
+    }
+    uint32_t prefix = 0u, mask = 0u;
+    int need = kk;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = digit_shift(pass);
+        const uint32_t dm = digit_mask(pass);
+        for (int j = tid; j < TOPK_BINS; j += NT) hist[j] = 0;
+        __syncthreads();
+        for (int i = tid; i < L; i += NT) {
+            const uint32_t u = score_key(s[i]);
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & dm], 1);
+        }
+        __syncthreads();
+        find_digit<NT>(hist, need, ws, sh);
+        prefix |= (uint32_t)sh[0] << shift;
+        mask |= dm << shift;
+        need = sh[1];
+        if (sh[2] == need) break;
+    }
+    const int seg = (L + NT - 1) / NT;
+    const int i0 = tid * seg, i1 = i0 + seg < L ? i0 + seg : L;
+    int gt = 0, eq = 0;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t m = score_key(s[i]) & mask;
+        gt += m > prefix;
+        eq += m == prefix;
+    }
+    int tot;
+    const int eq_before = block_exclusive_scan<NT>(eq, ws, &tot);
+    int take_eq = need - eq_before;
+    take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
+    int pos = block_exclusive_scan<NT>(gt + take_eq, ws, &tot);
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t m = score_key(s[i]) & mask;
+        if (m > prefix || (m == prefix && take_eq > 0)) {
+            if (m == prefix) --take_eq;
+            if (pos < kk) o[pos] = i + offset;
+            ++pos;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void check_idxs_kernel(const int32_t *__restrict__ idxs,
                                                          int64_t total, int64_t N,
                                                          int32_t *bad) {
@@ -1455,6 +1737,33 @@ const char *sparse_attn_plan_kernel(const sa_dims *d, int32_t num_splits) {
     const int di = d->D == 128 ? 0 : d->D == 256 ? 1 : 2;
     const int wi = w.ht == 1 ? (w.nhq == 4 ? 0 : 2) : 1;
     return names[di][wi];
+}
+
+int sparse_attn_topk(const float *scores, const int32_t *lens, int32_t Q, int32_t C, int32_t k,
+                     int32_t offset, int32_t *out, int64_t out_stride, hipStream_t stream) {
+    if (Q < 0 || C < 0 || k < 0 || out_stride < k) return SA_ERR_SHAPE;
+    if (Q == 0 || k == 0) return SA_OK;
+    if (out == nullptr || (scores == nullptr && C > 0)) return SA_ERR_NULL;
+    if (!aligned(out, 4) || !aligned(scores, 4) || !aligned(lens, 4)) return SA_ERR_ALIGN;
+    if ((int64_t)offset + C > 0x7FFFFFFF) return SA_ERR_SHAPE;
+    // keys held in registers up to 16384 candidates, else re-read from memory
+    const dim3 grid((unsigned)Q);
+    if (C <= 2048)
+        hipLaunchKernelGGL((topk_reg_kernel<256, 8>), grid, dim3(256), 0, stream, scores, lens, C, k,
+                           offset, out, out_stride);
+    else if (C <= 4096)
+        hipLaunchKernelGGL((topk_reg_kernel<256, 16>), grid, dim3(256), 0, stream, scores, lens, C, k,
+                           offset, out, out_stride);
+    else if (C <= 8192)
+        hipLaunchKernelGGL((topk_reg_kernel<512, 16>), grid, dim3(512), 0, stream, scores, lens, C, k,
+                           offset, out, out_stride);
+    else if (C <= 16384)
+        hipLaunchKernelGGL((topk_reg_kernel<1024, 16>), grid, dim3(1024), 0, stream, scores, lens, C,
+                           k, offset, out, out_stride);
+    else
+        hipLaunchKernelGGL(topk_long_kernel<256>, grid, dim3(256), 0, stream, scores, lens, C, k,
+                           offset, out, out_stride);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
 const char *sparse_attn_status_str(int status) {

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert set(names) == set(_lib.SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -178,3 +178,17 @@ def test_fp4_record_bytes_and_errors(L):
     assert f(rec=None) == SA_ERR_NULL
     assert f(rec=ctypes.c_void_p(0x10008)) == SA_ERR_ALIGN
     assert f(d=dims(D=100)) == SA_ERR_UNSUPPORTED
+
+
+def test_topk_argument_errors(L):
+    t = lambda scores=A, lens=None, Q=4, C=100, k=10, out=A2, stride=10: L.sparse_attn_topk(
+        scores, lens, Q, C, k, 0, out, stride, None)
+    assert t(Q=-1) == SA_ERR_SHAPE
+    assert t(k=-1) == SA_ERR_SHAPE
+    assert t(stride=9) == SA_ERR_SHAPE                       # rows would overlap
+    assert t(out=None) == SA_ERR_NULL
+    assert t(scores=None) == SA_ERR_NULL
+    assert t(out=ctypes.c_void_p(0x20002)) == SA_ERR_ALIGN
+    assert t(Q=0, out=None, scores=None) == SA_OK            # nothing to do
+    assert t(k=0, out=None) == SA_OK
+    assert L.sparse_attn_topk(A, None, 1, 2**31 - 5, 10, 100, A2, 10, None) == SA_ERR_SHAPE

@@ -402,6 +402,105 @@ def test_fp4_full_decode():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# ------------------------------------------------- top-k selection (the lists' compressed segment)
+
+@pytest.fixture(scope="module")
+def topk_ref():
+    import oracle
+    return oracle.topk_ref
+
+
+def test_topk_decode_shape_in_place(topk_ref):
+    # 64 queries x 8192 compressed scores -> 512 positions + 128 (the window),
+    # written straight into the compressed segment of [64, 1, 640] lists
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    rng = np.random.default_rng(40)
+    sc = rng.standard_normal((64, 1, 8192), dtype=np.float32)
+    lists = torch.full((64, 1, 640), 7, dtype=torch.int32, device="cuda")
+    api.topk(torch.from_numpy(sc).cuda(), 512, 128, out=lists[..., 128:])
+    torch.cuda.synchronize()
+    got = lists.cpu().numpy()
+    assert np.all(got[..., :128] == 7)                       # the window segment untouched
+    assert np.array_equal(got[:, 0, 128:], topk_ref(sc[:, 0], None, 512, 128))
+
+
+def test_topk_ties_and_special_values(topk_ref):
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    rng = np.random.default_rng(41)
+    sc = rng.integers(-3, 4, (50, 3000)).astype(np.float32)   # heavy ties
+    sc[rng.random(sc.shape) < 0.05] = np.nan
+    sc[rng.random(sc.shape) < 0.05] = -0.0
+    sc[rng.random(sc.shape) < 0.02] = np.inf
+    sc[rng.random(sc.shape) < 0.02] = -np.inf
+    got = api.topk(torch.from_numpy(sc).cuda(), 700, 5).cpu().numpy()
+    assert np.array_equal(got, topk_ref(sc, None, 700, 5))
+
+
+def test_topk_causal_visible_counts(topk_ref):
+    # prefill shape: query t sees floor((t+1)/2) of 2048 compressed positions
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    rng = np.random.default_rng(42)
+    T = 4096
+    sc = rng.standard_normal((T, 2048), dtype=np.float32)
+    lens = ((np.arange(T) + 1) // 2).astype(np.int32)
+    got = api.topk(torch.from_numpy(sc).cuda(), 512, 4096,
+                   lens=torch.from_numpy(lens).cuda()).cpu().numpy()
+    assert np.array_equal(got, topk_ref(sc, lens, 512, 4096))
+
+
+def test_topk_long_rows_and_edges(topk_ref):
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    rng = np.random.default_rng(43)
+    sc = rng.standard_normal((8, 65536), dtype=np.float32)       # rows re-read from memory
+    got = api.topk(torch.from_numpy(sc).cuda(), 512, 128).cpu().numpy()
+    assert np.array_equal(got, topk_ref(sc, None, 512, 128))
+    # every workgroup shape: odd row lengths (scalar loads), visible counts
+    # cut mid-thread, and rows past the register limit with counts
+    for Qk, Ck, kk in ((6, 12001, 512), (4, 16384, 2048), (7, 4093, 300), (3, 20000, 512)):
+        sc = rng.standard_normal((Qk, Ck), dtype=np.float32)
+        lens = rng.integers(0, Ck + 1, Qk).astype(np.int32)
+        lens[0] = Ck
+        got = api.topk(torch.from_numpy(sc).cuda(), kk, 0,
+                       lens=torch.from_numpy(lens).cuda()).cpu().numpy()
+        assert np.array_equal(got, topk_ref(sc, lens, kk, 0)), (Qk, Ck, kk)
+    small = rng.standard_normal((5, 37), dtype=np.float32)
+    for k in (0, 1, 36, 37, 60):
+        g = api.topk(torch.from_numpy(small).cuda(), k, 0).cpu().numpy()
+        assert np.array_equal(g, topk_ref(small, None, k, 0)), k
+
+
+def test_topk_feeds_attention(ref, topk_ref):
+    # end to end: scores -> compressed segment of the lists -> sparse_attn
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    rng = np.random.default_rng(44)
+    B, W, C, H, D = 4, 128, 1024, 64, 512
+    base = wl.make_random(240, B, 1, H, D, W + C, 256, p_unused=0.0)
+    sc = rng.standard_normal((B, 1, C), dtype=np.float32)
+    lists = np.full((B, 1, W + 256), -1, np.int32)
+    lists[..., :W] = np.arange(W)
+    lists_t = torch.from_numpy(lists).cuda()
+    api.topk(torch.from_numpy(sc).cuda(), 256, W, out=lists_t[..., W:])
+    exp_lists = lists.copy()
+    exp_lists[:, 0, W:] = topk_ref(sc[:, 0], None, 256, W)
+    torch.cuda.synchronize()
+    assert np.array_equal(lists_t.cpu().numpy(), exp_lists)
+    q, kv, sk, _ = to_dev(base)
+    # dense random rows for every position (the base workload stores only its own rows)
+    rows = torch.from_numpy(np.random.default_rng(45).standard_normal((B, W + C, D), dtype=np.float32))
+    kv_bits = wl.to_bf16_bits(rows.numpy())
+    kv_t = torch.from_numpy(kv_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    out = api.sparse_attn(q, kv_t, sk, lists_t, base.scale)
+    torch.cuda.synchronize()
+    got = wl.bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    exp = ref(base.q, kv_bits, base.sink, exp_lists, base.scale)
+    assert_close(got, exp, "top-k lists into sparse_attn")
+
+
 # --------------------------------------------------------- full-size workloads
 # Same launch configuration as bench.py: num_splits=0 (planned by the library).
 
