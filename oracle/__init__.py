@@ -9,6 +9,11 @@ from it.
 
 ``build()`` compiles the C source with gcc (-O2, OpenMP, no fast-math);
 ``sparse_attn_ref`` calls it through ctypes on numpy arrays.
+
+Parity unpinned: the pair layout of ``rotate_back`` (the pages call
+apply_rotary_emb on the output's rotary dims with inverse=True but do not
+show its body; the reading taken is DeepSeek's complex convention, consecutive
+elements 2i, 2i+1 as real and imaginary parts).  The rotation itself is pinned.
 """
 from __future__ import annotations
 
@@ -164,6 +169,34 @@ def topk_ref(scores, lens, k, offset):
         take = np.sort(order[:min(k, L)])
         out[qi, :len(take)] = take + offset
     return out
+
+
+def rotate_back(o, freqs, rd):
+    """The output's rotary dims rotated back (DeepSeek-V4.1 pages, "Output
+    projection" page, Attention.forward excerpt: apply_rotary_emb on
+    o[..., -rd:] with freqs_cis and inverse=True).  o is float64 [B, T, H, D];
+    freqs is float32 [T, rd/2, 2], the (cos, sin) of the angle of pair i at
+    position t (freqs_cis[t, i] as real and imaginary parts).  Reading: pair i
+    is the complex number o[..., D-rd+2i] + 1j * o[..., D-rd+2i+1], and the
+    inverse multiplies it by conj(freqs_cis[t, i]).  The first D - rd dims are
+    returned unchanged."""
+    o = np.array(o, dtype=np.float64, copy=True)
+    if rd == 0:
+        return o
+    D = o.shape[-1]
+    f = np.asarray(freqs, dtype=np.float64)
+    rot = f[..., 0] + 1j * f[..., 1]                      # freqs_cis [T, rd/2]
+    z = o[..., D - rd::2] + 1j * o[..., D - rd + 1::2]    # [B, T, H, rd/2]
+    z = z * np.conj(rot)[None, :, None, :]
+    o[..., D - rd::2] = z.real
+    o[..., D - rd + 1::2] = z.imag
+    return o
+
+
+def sparse_attn_rope_ref(q_bits, kv_bits, sink, idxs, scale, freqs, rd):
+    """sparse_attn followed by the inverse rotation of the output's last rd
+    dims (the two steps of the same excerpt, in that order)."""
+    return rotate_back(sparse_attn_ref(q_bits, kv_bits, sink, idxs, scale), freqs, rd)
 
 
 def ref_from_library(path):

@@ -154,3 +154,46 @@ def test_topk_oracle_pinned():
             lo = min((v for v in tv if v == v), default=None)
             hi = max((v for v in rest if v == v), default=None)
             assert lo is None or hi is None or lo >= hi
+
+
+def test_rotate_back_pinned():
+    """The inverse rotation of the output's rotary dims against what fixes a
+    rotation: zero angles change nothing, a quarter turn maps a pair (x, y)
+    to (y, -x) (multiplying x + iy by conj(i) = -i), every pair keeps its
+    length, the dims before the rotary part are untouched, and rotating back
+    by a then by b equals rotating back by a + b."""
+    import oracle
+    rng = np.random.default_rng(21)
+    B, T, H, D, rd = 2, 3, 4, 32, 8
+    o = rng.standard_normal((B, T, H, D))
+    zero = np.zeros((T, rd // 2, 2), np.float32)
+    zero[..., 0] = 1.0
+    assert np.array_equal(oracle.rotate_back(o, zero, rd), o)
+    quarter = np.zeros((T, rd // 2, 2), np.float32)
+    quarter[..., 1] = 1.0
+    got = oracle.rotate_back(o, quarter, rd)
+    exp = o.copy()
+    exp[..., D - rd::2] = o[..., D - rd + 1::2]
+    exp[..., D - rd + 1::2] = -o[..., D - rd::2]
+    assert np.array_equal(got, exp)
+    a = rng.uniform(-np.pi, np.pi, (T, rd // 2))
+    b = rng.uniform(-np.pi, np.pi, (T, rd // 2))
+    fa = np.stack([np.cos(a), np.sin(a)], -1)
+    fb = np.stack([np.cos(b), np.sin(b)], -1)
+    fab = np.stack([np.cos(a + b), np.sin(a + b)], -1)
+    ra = oracle.rotate_back(o, fa, rd)
+    assert np.array_equal(ra[..., :D - rd], o[..., :D - rd])
+    n0 = o[..., D - rd::2] ** 2 + o[..., D - rd + 1::2] ** 2
+    n1 = ra[..., D - rd::2] ** 2 + ra[..., D - rd + 1::2] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.rotate_back(ra, fb, rd), oracle.rotate_back(o, fab, rd),
+                               rtol=0, atol=1e-12)
+    # a single pair at position 1 with angle pi/3: (1, 0) -> (cos, -sin)
+    one = np.zeros((1, 2, 1, 8))
+    one[0, 1, 0, 6] = 1.0
+    f = np.zeros((2, 1, 2))
+    f[:, 0, 0] = 1.0
+    f[1, 0] = [np.cos(np.pi / 3), np.sin(np.pi / 3)]
+    r = oracle.rotate_back(one, f, 2)
+    np.testing.assert_allclose(r[0, 1, 0, 6:], [0.5, -np.sqrt(3) / 2], atol=1e-15)
+    assert np.all(r[0, 0] == 0) and np.all(r[0, 1, 0, :6] == 0)
