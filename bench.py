@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--kv-format", default="bf16", choices=["bf16", "fp4"],
                     help="fp4: also time the step with the compressed rows packed as FP4 "
                          "records (E2M1 codes, one E4M3 scale per 16) beside bf16 window rows")
+    ap.add_argument("--rope", action="store_true",
+                    help="also time the step with the output's inverse rotary step fused "
+                         "(sparse_attn_fwd_rope, rd=64) against sparse_attn + a torch rotation")
     ap.add_argument("--topk", action="store_true",
                     help="also time the top-k selection that fills the lists' compressed "
                          "segment (decode and causal prefill shapes) and decode top-k + attention")
@@ -307,6 +310,33 @@ def main():
             "note": "window rows bf16; compressed rows as FP4 records (E2M1 codes + one E4M3 "
                     "scale per 16 elements), expanded to bf16 in LDS"}
 
+
+    if args.rope:
+        # the output's last 64 dims rotated back (the step right after
+        # sparse_attn in the pages' forward), fused into the output rounding,
+        # against the unfused pair: sparse_attn, then a float32 complex
+        # rotation of o[..., -64:] in torch
+        rd = 64
+        fr = torch.from_numpy(wl.make_freqs(w.seed, w.T, rd)).to(dev)
+        fc = torch.view_as_complex(fr).conj()[None, :, None, :]
+
+        def fused(i):
+            api.sparse_attn_rope(qs[i], kvs[i], sink, idxs[i], w.scale, fr, rd, out=out,
+                                 num_splits=S, workspace=ws)
+
+        def unfused(i):
+            step(i)
+            x = out[..., -rd:].float().reshape(w.B, w.T, w.H, rd // 2, 2)
+            y = torch.view_as_real(torch.view_as_complex(x) * fc)
+            out[..., -rd:] = y.reshape(w.B, w.T, w.H, rd).to(torch.bfloat16)
+
+        ms_f = time_graph(fused)
+        ms_u = time_graph(unfused)
+        line["rope"] = {"rd": rd, "ms_per_step": round(ms_f, 5),
+                        "value": round(Qn / (ms_f * 1e-3), 1),
+                        "unfused_ms_per_step": round(ms_u, 5),
+                        "note": "inverse rotation of o[..., -64:] inside the output rounding "
+                                "(combine or epilogue) against sparse_attn + torch rotation"}
 
     if args.topk:
         # the compressed segment of the lists from indexer scores: the decode

@@ -93,6 +93,26 @@ int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int3
                     float scale, void *out, const sa_dims *d, int32_t num_splits,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The step followed by the inverse rotary step on the output (DeepSeek-V4.1
+ * pages, "Output projection" page, Attention.forward excerpt:
+ * apply_rotary_emb(o[..., -rd:], freqs_cis, True) right after sparse_attn),
+ * fused into the output's last rounding.
+ *   freqs  fp32 [T, rd/2, 2], 16-byte aligned: (cos, sin) of pair i at query
+ *          position t (freqs_cis[t, i] as real and imaginary parts; row t serves
+ *          query (b, t) of every sequence b, as the excerpt's slice does)
+ *   rd     0 (no rotation; freqs may be NULL) or a multiple of 8, <= D
+ * Pair i of head h of query (b, t) is the complex number
+ * x + iy = o[b,t,h,D-rd+2i] + i o[b,t,h,D-rd+2i+1]; it becomes
+ * (x + iy) * conj(cos + i sin), computed in float32 on the normalised output
+ * before the one bf16 rounding (the unfused pair of calls rounds twice).  The
+ * first D - rd dims equal sparse_attn_fwd's bit for bit.  SA_ERR_SHAPE for a
+ * bad rd, SA_ERR_NULL for freqs NULL with rd > 0, SA_ERR_ALIGN for freqs not
+ * 16-byte aligned; other arguments as sparse_attn_fwd. */
+int sparse_attn_fwd_rope(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                         float scale, const float *freqs, int32_t rd, void *out, const sa_dims *d,
+                         int32_t num_splits, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* The same step with the rows in two buffers instead of one concatenated kv
  * (DeepSeek-V4.1 pages, "Output projection" page, Attention.forward excerpt:
  * kv = cat([window_kv, compress_kv], dim=1), with compressed indices offset by

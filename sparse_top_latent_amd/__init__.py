@@ -4,7 +4,7 @@ The kernels live in libsparse_attn.so (C ABI: include/sparse_attn.h); this
 package holds the thin binding (``api``), the in-tree build (``build``) and
 the seeded input generators (``workloads``).
 """
-__all__ = ["sparse_attn", "sparse_attn_2src", "sparse_attn_2src_fp4", "fp4_record_bytes", "sparse_attn_partial", "sparse_attn_combine", "check_idxs", "topk",
+__all__ = ["sparse_attn", "sparse_attn_rope", "sparse_attn_2src", "sparse_attn_2src_fp4", "fp4_record_bytes", "sparse_attn_partial", "sparse_attn_combine", "check_idxs", "topk",
            "plan_splits", "plan_kernel", "workspace_bytes"]
 
 

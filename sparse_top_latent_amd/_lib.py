@@ -15,6 +15,7 @@ SYMBOLS = (
     "sparse_attn_plan_splits",
     "sparse_attn_workspace_bytes",
     "sparse_attn_fwd",
+    "sparse_attn_fwd_rope",
     "sparse_attn_fwd_2src",
     "sparse_attn_fwd_2src_fp4",
     "sparse_attn_fp4_record_bytes",
@@ -55,6 +56,8 @@ def lib():
         L.sparse_attn_workspace_bytes.restype = SZ
         L.sparse_attn_fwd.argtypes = [P, P, P, P, F, P, D, I32, P, SZ, P]
         L.sparse_attn_fwd.restype = ctypes.c_int
+        L.sparse_attn_fwd_rope.argtypes = [P, P, P, P, F, P, I32, P, D, I32, P, SZ, P]
+        L.sparse_attn_fwd_rope.restype = ctypes.c_int
         L.sparse_attn_fwd_2src.argtypes = [P, P, I32, P, I32, I32, P, P, F, P, D, I32, P, SZ, P]
         L.sparse_attn_fwd_2src.restype = ctypes.c_int
         L.sparse_attn_fwd_2src_fp4.argtypes = [P, P, I32, P, I32, I32, P, P, F, P, D, I32, P, SZ, P]

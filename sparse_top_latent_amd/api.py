@@ -102,6 +102,38 @@ def sparse_attn(q, kv, sink, idxs, scale: float, out=None, num_splits: int = 0,
     return out
 
 
+def sparse_attn_rope(q, kv, sink, idxs, scale: float, freqs, rd: int, out=None,
+                     num_splits: int = 0, workspace=None):
+    """sparse_attn followed by the inverse rotary step on the output's last rd
+    dims: pair i (dims D-rd+2i, D-rd+2i+1) of query (b, t) as a complex number
+    times the conjugate of freqs[t, i] (freqs: float32 [T, rd/2, 2] of
+    (cos, sin), e.g. torch.view_as_real of the complex freqs_cis slice), fused
+    into the output's rounding."""
+    _check_tensors(q, kv, sink, idxs)
+    dims = _dims(q, kv, idxs)
+    T, D = q.shape[1], q.shape[3]
+    if freqs is not None:
+        if freqs.dtype != torch.float32 or not freqs.is_contiguous() \
+                or tuple(freqs.shape) != (T, rd // 2, 2) or freqs.device != q.device:
+            raise ValueError("freqs must be a contiguous float32 [T, rd/2, 2] tensor on q's device")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    L = _lib.lib()
+    with torch.cuda.device(q.device):
+        need = int(L.sparse_attn_workspace_bytes(ctypes.byref(dims), num_splits))
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = L.sparse_attn_fwd_rope(_ptr(q), _ptr(kv), _ptr(sink), _ptr(idxs),
+                                    ctypes.c_float(scale), _ptr(freqs), rd, _ptr(out),
+                                    ctypes.byref(dims), num_splits, _ptr(workspace), ws_bytes,
+                                    _stream(q.device))
+    _lib.check(rc, "sparse_attn_fwd_rope")
+    return out
+
+
 def sparse_attn_2src(q, kv_win, kv_cmp, W: int, N: int, sink, idxs, scale: float, out=None,
                      num_splits: int = 0, workspace=None):
     """sparse_attn over rows held in two buffers: list entry j < W is kv_win[b, j],

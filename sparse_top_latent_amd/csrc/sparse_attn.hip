@@ -72,7 +72,22 @@ struct FwdParams {
     int32_t T, H, K;
     int32_t S, HG, units, per_xcd, bs;  // see unit_of
     float qk_scale_log2;  // scale * log2(e)
+    // f3: the output's last rd dims rotated back, pair i of query (b, t) by
+    // rope[t, i] = (cos, sin) (rd = 0: none)
+    const float *rope;
+    int32_t rd;
 };
+
+// f3: inverse rotary step on two pairs (x0, y0), (x1, y1) of an output row
+// (DeepSeek-V4.1 pages, "Output projection" page, Attention.forward excerpt:
+// apply_rotary_emb on o[..., -rd:] with inverse=True).  A pair is the complex
+// number x + iy, multiplied by the conjugate of freqs_cis = cs.x + i cs.y
+// (and cs.z + i cs.w for the second pair).
+__device__ __forceinline__ void rotate_back2(float &x0, float &y0, float &x1, float &y1, float4 cs) {
+    const float a0 = x0 * cs.x + y0 * cs.y, b0 = y0 * cs.x - x0 * cs.y;
+    const float a1 = x1 * cs.z + y1 * cs.w, b1 = y1 * cs.z - x1 * cs.w;
+    x0 = a0, y0 = b0, x1 = a1, y1 = b1;
+}
 
 // Row swizzle of the 16-byte chunks of a 16-bit row in an LDS staging area
 // (the epilogue's output rows): chunk c of row r lives at position
@@ -254,8 +269,13 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
             for (int u = 0; u < DTH; ++u) {
                 const int col = dh * (D / 2) + 16 * u + 4 * g;  // first of 4 columns
                 const int pos = (col >> 3) ^ swz<C16>(hl);
-                const u32x2_t w = {pack2_bf16(o[t][u][0] * inv, o[t][u][1] * inv),
-                                   pack2_bf16(o[t][u][2] * inv, o[t][u][3] * inv)};
+                float v0 = o[t][u][0] * inv, v1 = o[t][u][1] * inv;
+                float v2 = o[t][u][2] * inv, v3 = o[t][u][3] * inv;
+                if (col >= D - p.rd) {  // rotary dims: pairs (col, col+1), (col+2, col+3)
+                    const int64_t pr = (int64_t)(qi % p.T) * (p.rd / 2) + (col - (D - p.rd)) / 2;
+                    rotate_back2(v0, v1, v2, v3, *(const float4 *)(p.rope + 2 * pr));
+                }
+                const u32x2_t w = {pack2_bf16(v0, v1), pack2_bf16(v2, v3)};
                 *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
             }
         } else {
@@ -956,7 +976,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                                                       const float *__restrict__ ws_x,
                                                       const float *__restrict__ sink,
                                                       uint16_t *__restrict__ out, int64_t QH,
-                                                      int H, int S, int per_xcd) {
+                                                      int H, int S, int per_xcd,
+                                                      const float *__restrict__ rope, int rd,
+                                                      int T) {
     constexpr int LPR = D / 8;       // lanes per row
     constexpr int RPW = 64 / LPR;    // rows per wave
     constexpr int RWG = 4 * RPW;     // rows per workgroup
@@ -984,6 +1006,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     for (int j = 0; j < SB; ++j)
         v[j] = ok && j < S ? *(const u32x4_t *)(ws_o + (slot0 + (int64_t)j * H) * D + c8)
                            : u32x4_t{0, 0, 0, 0};
+    // rotary dims: the (cos, sin) of the lane's four pairs
+    const bool rot = ok && c8 >= D - rd;
+    float4 cs0 = {1.f, 0.f, 1.f, 0.f}, cs1 = cs0;
+    if (rot) {
+        const float *f = rope + 2 * ((int64_t)(qi % T) * (rd / 2) + (c8 - (D - rd)) / 2);
+        cs0 = *(const float4 *)f;
+        cs1 = *(const float4 *)(f + 4);
+    }
     // lane sl holds the scalars of splits sl, sl + LPR, ...
     float mj[SPL], lj[SPL], x0[SPL], x1[SPL];
 #pragma unroll
@@ -1043,6 +1073,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                 }
             }
         }
+    }
+    if (rot) {
+        rotate_back2(acc[0], acc[1], acc[2], acc[3], cs0);
+        rotate_back2(acc[4], acc[5], acc[6], acc[7], cs1);
     }
     if (ok) {
         const u32x4_t w = {pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]),
@@ -1434,7 +1468,8 @@ hipError_t launch_fwd_d(WgShape w, const FwdParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
-                          const void *ws, const WsLayout &L, hipStream_t stream) {
+                          const void *ws, const WsLayout &L, hipStream_t stream,
+                          const float *rope = nullptr, int rd = 0) {
     const int64_t QH = queries(d) * d->H;
     const int rwg = 4 * (64 / (d->D / 8));  // rows per workgroup
     const int64_t wgs = (QH + rwg - 1) / rwg;
@@ -1446,9 +1481,9 @@ hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
     const float *wx = (const float *)((const uint8_t *)ws + L.x_off);
     uint16_t *o = (uint16_t *)out;
     switch (d->D) {
-        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd); break;
-        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd); break;
-        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd); break;
+        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
+        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
+        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
     }
     return hipGetLastError();
 }
@@ -1588,16 +1623,28 @@ size_t sparse_attn_workspace_bytes(const sa_dims *d, int32_t num_splits) {
 int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int32_t *idxs,
                     float scale, void *out, const sa_dims *d, int32_t num_splits, void *workspace,
                     size_t workspace_bytes, hipStream_t stream) {
+    return sparse_attn_fwd_rope(q, kv, sink, idxs, scale, nullptr, 0, out, d, num_splits,
+                                workspace, workspace_bytes, stream);
+}
+
+int sparse_attn_fwd_rope(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                         float scale, const float *freqs, int32_t rd, void *out, const sa_dims *d,
+                         int32_t num_splits, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
     int S = 1;
     int rc = check_common(q, kv, idxs, d, num_splits, workspace, workspace_bytes, false, &S);
     if (rc != SA_OK) return rc;
+    if (rd < 0 || rd % 8 != 0 || rd > d->D) return SA_ERR_SHAPE;
     if (queries(d) == 0) return SA_OK;
-    if (out == nullptr) return SA_ERR_NULL;
-    if (!aligned(out, 16) || !aligned(sink, 4)) return SA_ERR_ALIGN;
+    if (out == nullptr || (rd > 0 && freqs == nullptr)) return SA_ERR_NULL;
+    if (!aligned(out, 16) || !aligned(sink, 4) || !aligned(freqs, 16)) return SA_ERR_ALIGN;
     if (!units_fit(d, S)) return SA_ERR_SHAPE;
-    const FwdParams p = make_params(q, kv, sink, idxs, scale, out, d, S, workspace);
+    FwdParams p = make_params(q, kv, sink, idxs, scale, out, d, S, workspace);
+    p.rope = rd > 0 ? freqs : nullptr;
+    p.rd = rd;
     if (run_fwd(p, d->D, d->H, stream) != hipSuccess) return SA_ERR_HIP;
-    if (S > 1 && launch_combine(d, S, sink, out, workspace, ws_layout(d, S), stream) != hipSuccess)
+    if (S > 1 && launch_combine(d, S, sink, out, workspace, ws_layout(d, S), stream, p.rope,
+                                rd) != hipSuccess)
         return SA_ERR_HIP;
     return SA_OK;
 }

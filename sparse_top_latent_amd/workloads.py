@@ -268,6 +268,18 @@ def make_random(seed: int, B: int, T: int, H: int, D: int, N: int, K: int,
     return _finish(f"random{seed}", B, T, H, D, N, K, sc, seed, idxs)
 
 
+def make_freqs(seed: int, T: int, rd: int, theta: float = 10000.0) -> np.ndarray:
+    """Synthetic rotary table, float32 [T, rd/2, 2] of (cos, sin): pair i at
+    position p0 + t turns by (p0 + t) * theta^(-2i/rd), with the start
+    position p0 drawn from [0, 65536) (tensor id 5 of the seed).  The pages
+    build theirs with YaRN scaling, which only changes the angles."""
+    p0 = int(_rng(seed, 5).integers(0, 65536))
+    pos = np.arange(p0, p0 + T, dtype=np.float64)[:, None]
+    inv = theta ** (-np.arange(0, rd, 2, dtype=np.float64) / rd)[None, :]
+    ang = pos * inv
+    return np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)
+
+
 def make_fp4_records(seed: int, B: int, rows: int, D: int, R: int) -> np.ndarray:
     """Synthetic packed FP4 rows (uint8 [B, rows, R]): uniform E2M1 codes in the
     first D/2 bytes, then D/16 positive E4M3 scales with exponent field 4..5

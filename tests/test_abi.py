@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert set(names) == set(_lib.SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -178,6 +178,21 @@ def test_fp4_record_bytes_and_errors(L):
     assert f(rec=None) == SA_ERR_NULL
     assert f(rec=ctypes.c_void_p(0x10008)) == SA_ERR_ALIGN
     assert f(d=dims(D=100)) == SA_ERR_UNSUPPORTED
+
+
+def test_rope_argument_errors(L):
+    # rotary table: rd a multiple of 8 within D, freqs present and 16-byte aligned
+    F = ctypes.c_void_p(0x20000)
+    r = lambda rd=64, freqs=F, d=None: L.sparse_attn_fwd_rope(
+        A, A, None, A, ctypes.c_float(0.1), freqs, rd, A2, dims() if d is None else d, 1, None,
+        0, None)
+    assert r(rd=-8) == SA_ERR_SHAPE
+    assert r(rd=12) == SA_ERR_SHAPE
+    assert r(rd=520) == SA_ERR_SHAPE          # dims() has D = 512
+    assert r(freqs=None) == SA_ERR_NULL
+    assert r(freqs=ctypes.c_void_p(0x20008)) == SA_ERR_ALIGN
+    assert r(d=dims(B=0)) == SA_OK
+    assert r(d=dims(B=0), rd=12) == SA_ERR_SHAPE
 
 
 def test_topk_argument_errors(L):

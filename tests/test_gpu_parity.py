@@ -402,6 +402,66 @@ def test_fp4_full_decode():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# ------------------------------------------ the output's inverse rotary step, fused
+
+def run_rope(w, freqs, rd, S=0):
+    """(fused rope output, plain sparse_attn output) as bf16 bit patterns."""
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    q, kv, sk, idx = to_dev(w)
+    f = None if freqs is None else torch.from_numpy(freqs).cuda()
+    out = api.sparse_attn_rope(q, kv, sk, idx, w.scale, f, rd, num_splits=S)
+    plain = api.sparse_attn(q, kv, sk, idx, w.scale, num_splits=S)
+    torch.cuda.synchronize()
+    return (out.view(torch.int16).cpu().numpy().view(np.uint16),
+            plain.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def check_rope(w, rd, S, what):
+    import oracle
+    freqs = wl.make_freqs(w.seed, w.T, rd)
+    bits, pbits = run_rope(w, freqs, rd, S)
+    # the dims before the rotary part are sparse_attn's, bit for bit
+    assert np.array_equal(bits[..., :w.D - rd], pbits[..., :w.D - rd]), what
+    got = wl.bf16_bits_to_f32(bits).astype(np.float64)
+    exp = oracle.sparse_attn_rope_ref(w.q, w.kv_host(), w.sink, w.idxs, w.scale, freqs, rd)
+    assert_close(got, exp, what)
+
+
+@pytest.mark.parametrize("H,D,rd,S", [(8, 128, 32, 1), (8, 128, 32, 3), (16, 256, 8, 2),
+                                      (64, 512, 64, 1), (64, 512, 64, 4), (4, 128, 128, 1)])
+def test_rope_fused(H, D, rd, S):
+    w = wl.make_random(250 + D + S, 2, 5, H, D, 300, 96)
+    check_rope(w, rd, S, f"rope H={H} D={D} rd={rd} S={S}")
+
+
+def test_rope_many_query_path():
+    w = wl.make_random(260, 2, many_query_T(), 64, 512, 160, 75, p_unused=0.3)
+    for S in (1, 2):
+        check_rope(w, 64, S, f"rope many-query S={S}")
+
+
+def test_rope_zero_is_plain():
+    w = wl.make_random(261, 2, 3, 16, 256, 200, 64)
+    for S in (1, 3):
+        bits, pbits = run_rope(w, None, 0, S)
+        assert np.array_equal(bits, pbits)
+
+
+def test_rope_full_decode(ref):
+    import oracle
+    w = wl.make("decode")
+    freqs = wl.make_freqs(w.seed, w.T, 64)
+    bits, pbits = run_rope(w, freqs, 64, 0)
+    assert np.array_equal(bits[..., :w.D - 64], pbits[..., :w.D - 64])
+    got = wl.bf16_bits_to_f32(bits).astype(np.float64)
+    exps = []
+    for b in range(w.B):
+        q1, kv1, i1 = w.query_slice(b, 0)
+        exps.append(oracle.sparse_attn_rope_ref(q1, kv1, w.sink, i1, w.scale, freqs, 64)[0, 0])
+    assert_close(got[:, 0], np.stack(exps), "rope decode every query")
+
+
 # ------------------------------------------------- top-k selection (the lists' compressed segment)
 
 @pytest.fixture(scope="module")
