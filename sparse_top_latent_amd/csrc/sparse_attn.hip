@@ -157,10 +157,17 @@ __device__ int compact_list(const LDS_AS int32_t *lst, int K, int64_t N, int32_t
     int v[MAXR];
     uint64_t mask[MAXR];
     int total = 0;
+    // every read is issued before any is used (indices clamped into the
+    // list, the entries beyond it discarded after)
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
         const int k = k0 + r * 64 + lane;
-        v[r] = r * 64 < seg && k < K ? lst[k] : -1;
+        v[r] = lst[k < K ? k : (K > 0 ? K - 1 : 0)];
+    }
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+        const int k = k0 + r * 64 + lane;
+        if (!(r * 64 < seg && k < K)) v[r] = -1;
         mask[r] = __ballot(v[r] >= 0 && (int64_t)v[r] < N);
         total += __popcll(mask[r]);
     }
@@ -179,7 +186,7 @@ __device__ int compact_list(const LDS_AS int32_t *lst, int K, int64_t N, int32_t
         base += __popcll(mask[r]);
     }
     __syncthreads();
-    return n;
+    return __builtin_amdgcn_readfirstlane(n);
 }
 
 // One LDS-DMA wave instruction: every lane fetches 16 bytes from its own
@@ -512,8 +519,8 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 
     // a1: decode and compact the list, then take this split's slice.
     const int n = compact_list<NT>(raw, p.K, p.N, list, cnt);
-    const int lo = (int)(((int64_t)n * s) / p.S);
-    const int hi = (int)(((int64_t)n * (s + 1)) / p.S);
+    const int lo = (n * s) / p.S;  // n <= LIST_CAP and s < MAX_SPLITS: no overflow
+    const int hi = (n * (s + 1)) / p.S;
     const int nchunks = (hi - lo + KC - 1) / KC;
 
     // a2: gather the rows of chunk c into ring slot c % NBUF with LDS-DMA.
@@ -597,23 +604,34 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         if (FP4) expand_fp4<D, NT, KC>((LDS_AS uint8_t *)T, RS, p.rec2, list, lo + c * KC, hi, p.W);
 
         // a4: partial S^T[j, h] over this wave's half of d (two 16-row tiles
-        // x HT head tiles; each K operand feeds HT MFMAs).
+        // x HT head tiles; each K operand feeds HT MFMAs).  Software-pipelined
+        // by hand: operand i + QKP is requested right after the MFMAs of
+        // operand i, and the scheduling barriers keep that order (left alone,
+        // the scheduler requests each operand next to its MFMA and the LDS
+        // latency is exposed on every one).
         f32x4_t sacc[2][HT];
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
             for (int t = 0; t < HT; ++t) sacc[jt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        {
+            constexpr int QKP = 4, NQK = 2 * DSH;
+            auto kload = [&](int i) {  // operand i: k-step i/2, row tile i%2
+                const int r = (i & 1) * 16 + li;
+                const int pos = 4 * (dh * DSH + (i >> 1)) + g;
+                return __builtin_bit_cast(bf16x8_t, *(const LDS_AS u32x4_t *)(T + r * RS + pos * 16));
+            };
+            bf16x8_t ka[QKP];
 #pragma unroll
-        for (int k = 0; k < DSH; ++k) {
+            for (int i = 0; i < QKP; ++i) ka[i] = kload(i);
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                const int r = jt * 16 + li;
-                const int pos = 4 * (dh * DSH + k) + g;
-                const bf16x8_t a = __builtin_bit_cast(
-                    bf16x8_t, *(const LDS_AS u32x4_t *)(T + r * RS + pos * 16));
+            for (int i = 0; i < NQK; ++i) {
 #pragma unroll
                 for (int t = 0; t < HT; ++t)
-                    sacc[jt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[t][k], sacc[jt][t], 0, 0, 0);
+                    sacc[i & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i % QKP], qf[t][i >> 1],
+                                                                             sacc[i & 1][t], 0, 0, 0);
+                if (i + QKP < NQK) ka[i % QKP] = kload(i + QKP);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // the pair adds its two halves (a + b == b + a, so both waves agree)
@@ -680,20 +698,29 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         // 4g + i/4 (and +16), columns 16t + 4(i%4) .. +3; the load hands lane i
         // column 16t + i of rows 4g..4g+3, matching the weight slots
         // j = 4g + e and 16 + 4g + e.  Each V operand feeds HT MFMAs.
+        // (pipelined by hand like QK^T: transpose pair u + PVP is requested
+        // right after the MFMAs of pair u)
         {
+            constexpr int PVP = 4;
             const int r0 = 4 * g + (li >> 2);
             const LDS_AS uint8_t *R0 = T + r0 * RS + (li & 3) * 8;
             const LDS_AS uint8_t *R1 = R0 + 16 * RS;
-#pragma unroll
-            for (int u = 0; u < DTH; ++u) {
-                const int tt = dh * DTH + u;
-                const int pos = tt * 32;
+            auto vload = [&](int u) {
+                const int pos = (dh * DTH + u) * 32;
                 const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R0 + pos));
                 const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R1 + pos));
-                const bf16x8_t a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            bf16x8_t va[PVP];
+#pragma unroll
+            for (int u = 0; u < PVP; ++u) va[u] = vload(u);
+#pragma unroll
+            for (int u = 0; u < DTH; ++u) {
 #pragma unroll
                 for (int t = 0; t < HT; ++t)
-                    o[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[t], o[t][u], 0, 0, 0);
+                    o[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u % PVP], pb[t], o[t][u], 0, 0, 0);
+                if (u + PVP < DTH) va[u % PVP] = vload(u + PVP);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -769,8 +796,8 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 
     // a1: decode and compact the list (in place), then take this split's slice.
     const int n = compact_list<NT>((const LDS_AS int32_t *)list, p.K, p.N, list, cnt);
-    const int lo = (int)(((int64_t)n * s) / p.S);
-    const int hi = (int)(((int64_t)n * (s + 1)) / p.S);
+    const int lo = (n * s) / p.S;  // n <= LIST_CAP and s < MAX_SPLITS: no overflow
+    const int hi = (n * (s + 1)) / p.S;
     const int nchunks = (hi - lo + KC - 1) / KC;
 
     // a2: chunk c (KC rows) into ring slot c % NB, one row per DMA
