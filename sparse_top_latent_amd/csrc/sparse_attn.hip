@@ -517,48 +517,80 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QIW) : "memory");
     __syncthreads();
 
+    // a2: the wave's k-th row of chunk c into ring slot c % NBUF with LDS-DMA.
+    // Each wave instruction moves one row: lane l < D/8 fetches its 16 bytes
+    // and lands at byte 16*l of the row's padded slot (an FP4 record, FP4
+    // build and rows >= W: lanes < rec2/16, at the tail of the slot).
+    auto dma_row = [&](int c, int k, int rw) {
+        LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (k * NW + wid) * RS;
+        if (!FP4 || rw < p.W) {
+            if (CPR == 64 || lane < CPR)
+                lds_dma16((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8, (LDS_AS void *)dst);
+        } else if (lane * 16 < p.rec2) {
+            lds_dma16(recb + (int64_t)rw * p.rec2 + lane * 16, (LDS_AS void *)(dst + RS - p.rec2));
+        }
+    };
+
+    // Chunk 0 ahead of the compaction: the rows it holds when every entry is
+    // valid (this split's slice K*s/S .. K*(s+1)/S of the raw list) are
+    // requested now; once the list is compacted each wave requests again only
+    // the rows whose number differs.  A later DMA into the same LDS row lands
+    // after the earlier one, and every later wait only lets younger loads
+    // remain, so the extra requests need no wait of their own.  Raw entries
+    // that are not rows (< 0 or >= N) are never fetched.
+    int spec[IPW];
+    {
+        const int slo = (p.K * s) / p.S, shi = (p.K * (s + 1)) / p.S;  // K <= LIST_CAP
+#pragma unroll
+        for (int k = 0; k < IPW; ++k) {
+            const int e = slo + k * NW + wid;
+            const int v = slo < shi ? raw[e < shi ? e : slo] : -1;
+            const int rw = __builtin_amdgcn_readfirstlane(v);
+            spec[k] = rw >= 0 && (int64_t)rw < p.N ? rw : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < IPW; ++k)
+            if (spec[k] >= 0) dma_row(0, k, spec[k]);
+    }
+
     // a1: decode and compact the list, then take this split's slice.
     const int n = compact_list<NT>(raw, p.K, p.N, list, cnt);
     const int lo = (n * s) / p.S;  // n <= LIST_CAP and s < MAX_SPLITS: no overflow
     const int hi = (n * (s + 1)) / p.S;
     const int nchunks = (hi - lo + KC - 1) / KC;
 
-    // a2: gather the rows of chunk c into ring slot c % NBUF with LDS-DMA.
-    // Each wave instruction moves one row: lane l < D/8 fetches its 16 bytes
-    // and lands at byte 16*l of the row's padded slot.  Tail slots repeat the
-    // chunk's first row; their scores are masked to -inf below.  All row
-    // numbers are read from the list before the first DMA is issued: the DMA
-    // asm orders memory, so interleaving them would put one LDS round trip in
-    // front of every DMA.
-    auto stage = [&](int c) {
+    // Tail slots repeat the chunk's first row; their scores are masked to
+    // -inf below.  All row numbers are read from the list before the first
+    // DMA is issued: the DMA asm orders memory, so interleaving them would put
+    // one LDS round trip in front of every DMA.
+    auto chunk_rows = [&](int c, int (&row)[IPW]) {
         const int e0 = lo + c * KC;
-        uint8_t *buf = &tile[c % NBUF][0];
-        int row[IPW];
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
             const int e = e0 + k * NW + wid;
-            row[k] = list[e < hi ? e : e0];
-        }
-#pragma unroll
-        for (int k = 0; k < IPW; ++k) {
-            const int r = k * NW + wid;
-            // the row number is wave-uniform: a scalar branch, one DMA either way
-            const int rw = __builtin_amdgcn_readfirstlane(row[k]);
-            if (!FP4 || rw < p.W) {
-                if (CPR == 64 || lane < CPR)
-                    lds_dma16((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8,
-                              (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS));
-            } else if (lane * 16 < p.rec2) {
-                lds_dma16(recb + (int64_t)rw * p.rec2 + lane * 16,
-                          (LDS_AS void *)((LDS_AS uint8_t *)buf + r * RS + RS - p.rec2));
-            }
+            // the row number is wave-uniform: scalar branches, one DMA per row
+            row[k] = __builtin_amdgcn_readfirstlane(list[e < hi ? e : e0]);
         }
     };
-    if (nchunks > 0) stage(0);
+    auto stage = [&](int c) {
+        int row[IPW];
+        chunk_rows(c, row);
+#pragma unroll
+        for (int k = 0; k < IPW; ++k) dma_row(c, k, row[k]);
+    };
+    if (nchunks > 0) {
+        int row[IPW];
+        chunk_rows(0, row);
+#pragma unroll
+        for (int k = 0; k < IPW; ++k)
+            if (row[k] != spec[k]) dma_row(0, k, row[k]);
+    }
 
-    // q of this wave has landed once only chunk 0 is pending; move it to the
-    // MFMA B operands qf[t][k] = q[hw0 + 16t + li, dh*D/2 + 32k + 8g .. +7]
-    // (zero for heads beyond H), then free slots 1-2 for chunks 1 and 2.
+    // q of this wave has landed once only chunk 0 is pending (at least IPW
+    // requests, each row once or twice); move it to the MFMA B operands
+    // qf[t][k] = q[hw0 + 16t + li, dh*D/2 + 32k + 8g .. +7] (zero for heads
+    // beyond H), then free slots 1-2 for chunks 1 and 2.  Without chunks,
+    // every request (the early ones of chunk 0 included) is waited for.
     if (nchunks > 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     bf16x8_t qf[HT][DSH];
