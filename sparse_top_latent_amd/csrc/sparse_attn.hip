@@ -625,11 +625,24 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     LDS_AS f32x4_t *xmine = (LDS_AS f32x4_t *)&xbuf[wid][0][lane];
     const LDS_AS f32x4_t *xpeer = (const LDS_AS f32x4_t *)&xbuf[wid ^ 1][0][lane];
 
+    // The loop requests chunk c + NBUF - 1 during chunk c's QK^T, one DMA
+    // every few MFMAs: LDS-DMA is throttled at issue per compute unit, and a
+    // burst of requests would hold the issuing waves back before their MFMAs.
+    // Its row numbers are read a chunk ahead (lane k holds the wave's k-th),
+    // so requesting one only moves it to an SGPR.
+    auto rows_of = [&](int c) {
+        const int e0 = lo + c * KC;
+        const int e = e0 + (lane % IPW) * NW + wid;
+        return list[e < hi ? e : e0];
+    };
+    int next_rows = NBUF - 1 < nchunks ? rows_of(NBUF - 1) : 0;
     for (int c = 0; c < nchunks; ++c) {
         // chunk c has landed once at most `ahead` later chunks are pending
         wait_vm_ahead<IPW, NBUF - 2>(min(NBUF - 2, nchunks - 1 - c));
         __syncthreads();
-        if (c + NBUF - 1 < nchunks) stage(c + NBUF - 1);
+        // slot (c + NBUF - 1) % NBUF was last read by chunk c - 1, which every
+        // wave finished before the barrier above
+        const bool do_stage = c + NBUF - 1 < nchunks;
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NBUF][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
@@ -663,9 +676,15 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
                     sacc[i & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i % QKP], qf[t][i >> 1],
                                                                              sacc[i & 1][t], 0, 0, 0);
                 if (i + QKP < NQK) ka[i % QKP] = kload(i + QKP);
+                if (do_stage) {  // DMAs k in [i*IPW/NQK, (i+1)*IPW/NQK): spread evenly
+#pragma unroll
+                    for (int k = i * IPW / NQK; k < (i + 1) * IPW / NQK; ++k)
+                        dma_row(c + NBUF - 1, k, __builtin_amdgcn_readlane(next_rows, k));
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if (do_stage && c + NBUF < nchunks) next_rows = rows_of(c + NBUF);
         // the pair adds its two halves (a + b == b + a, so both waves agree)
 #pragma unroll
         for (int t = 0; t < HT; ++t) {
