@@ -473,14 +473,13 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     const uint16_t *kva = p.kv + (int64_t)b * p.rows_a * D;
     const uint16_t *kvb2 = p.kv2 + ((int64_t)b * p.rows_b - p.W) * D;
     const uint8_t *recb = (const uint8_t *)p.kv2 + ((int64_t)b * p.rows_b - p.W) * p.rec2;
-    static_assert(NBUF == 4, "the prologue stages q in ring slots 1-2 and the list in slot 3");
+    static_assert(NBUF == 4, "the prologue stages the list in slot 3");
 
-    // Prologue.  The index list and q come in through LDS-DMA too, so every
-    // wait of the prologue and the ring is one of ours and the first row
-    // chunk is requested as soon as the list is compacted.  Per wave, in
-    // issue order: its share of the raw list (4 bytes per lane, into slot 3),
-    // its q block (QIW instructions, into slots 1-2), chunk 0, then chunks
-    // 1 and 2 once q has been read out of slots 1-2.
+    // Prologue.  Per wave, in issue order: its share of the raw list (LDS-DMA,
+    // 4 bytes per lane, into slot 3), its q (ordinary loads straight into the
+    // MFMA B operands: LDS-DMA is throttled at issue per compute unit, and q
+    // would queue 64 KB ahead of the first rows), then chunk 0 as soon as the
+    // list has landed.
     LDS_AS int32_t *raw = (LDS_AS int32_t *)&tile[3][0];
     {
         const int32_t *lst = p.idxs + (int64_t)qi * p.K;
@@ -490,31 +489,18 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             if (k < p.K) lds_dma4(lst + k, raw + i * 64);
         }
     }
-    // a3: this wave's HW heads x D/2 of q: head row hh of the block is D
-    // bytes at qstage + hh*D; its 16-byte chunk c sits at c ^ qswz(hh).
-    constexpr int QC = D / 16;                   // 16-byte chunks per half row
-    constexpr int HPI = 64 / QC;                 // half rows per DMA instruction
-    constexpr int QIW = HW / HPI;                // q DMA instructions per wave
-    static_assert(NW * HW * D <= 2 * KC * RS, "q of the workgroup fits ring slots 1-2");
-    auto qswz = [](int hh) {
-        return QC >= 32 ? (2 * hh) & 31 : (2 * (hh / (32 / QC))) & (QC - 1);
-    };
-    LDS_AS uint8_t *qstage = (LDS_AS uint8_t *)&tile[1][0] + wid * (HW * D);
-    {
+    // a3: qf[t][k] = q[hw0 + 16t + li, dh*D/2 + 32k + 8g .. +7]; heads beyond
+    // H read head 0 (in bounds) and are zeroed once q has landed
+    bf16x8_t qf[HT][DSH];
 #pragma unroll
-        for (int k = 0; k < QIW; ++k) {
-            const int hh = k * HPI + lane / QC;
-            const int pos = lane % QC;
-            // heads beyond H read head 0 (in bounds); their q is zeroed below.
-            // Every wave issues exactly QIW instructions: the waits count them.
-            const int hsrc = hw0 + hh < p.H ? hw0 + hh : 0;
-            const uint16_t *src = p.q + ((int64_t)qi * p.H + hsrc) * D + dh * (D / 2) +
-                                  ((pos ^ qswz(hh)) << 3);
-            lds_dma16(src, qstage + k * 1024);
-        }
+    for (int t = 0; t < HT; ++t) {
+        const int h = hw0 + 16 * t + li;
+        const uint16_t *qrow = p.q + ((int64_t)qi * p.H + (h < p.H ? h : 0)) * D + dh * (D / 2) + 8 * g;
+#pragma unroll
+        for (int k = 0; k < DSH; ++k) qf[t][k] = *(const bf16x8_t *)(qrow + 32 * k);
     }
-    // the raw list of this wave has landed once only its q DMAs are pending
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QIW) : "memory");
+    // the raw list of this wave has landed once only its q loads are pending
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HT * DSH) : "memory");
     __syncthreads();
 
     // a2: the wave's k-th row of chunk c into ring slot c % NBUF with LDS-DMA.
@@ -586,29 +572,18 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             if (row[k] != spec[k]) dma_row(0, k, row[k]);
     }
 
-    // q of this wave has landed once only chunk 0 is pending (at least IPW
-    // requests, each row once or twice); move it to the MFMA B operands
-    // qf[t][k] = q[hw0 + 16t + li, dh*D/2 + 32k + 8g .. +7] (zero for heads
-    // beyond H), then free slots 1-2 for chunks 1 and 2.  Without chunks,
-    // every request (the early ones of chunk 0 included) is waited for.
-    if (nchunks > 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    bf16x8_t qf[HT][DSH];
+    // Chunk 0 and q (and any early request) have landed once nothing is
+    // pending; the wait goes through the builtin so that the compiler knows
+    // q is in its registers.  Chunks 1 and 2 are requested inside the first
+    // QK^T (below).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
-        const int hh = 16 * t + li;
-        const bool ok = hw0 + hh < p.H;
+        if (hw0 + 16 * t + li >= p.H) {
 #pragma unroll
-        for (int k = 0; k < DSH; ++k) {
-            const int c = 4 * k + g;
-            u32x4_t v = *(const LDS_AS u32x4_t *)(qstage + hh * D + ((c ^ qswz(hh)) << 4));
-            if (!ok) v = u32x4_t{0, 0, 0, 0};
-            qf[t][k] = __builtin_bit_cast(bf16x8_t, v);
+            for (int k = 0; k < DSH; ++k) qf[t][k] = bf16x8_t{};
         }
     }
-    __syncthreads();
-    if (1 < nchunks) stage(1);
-    if (2 < nchunks) stage(2);
 
     // Softmax state of head hw0 + 16t + li (log2 units), identical in both
     // waves of the pair.  The sink is folded in by the epilogue.
@@ -625,24 +600,28 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     LDS_AS f32x4_t *xmine = (LDS_AS f32x4_t *)&xbuf[wid][0][lane];
     const LDS_AS f32x4_t *xpeer = (const LDS_AS f32x4_t *)&xbuf[wid ^ 1][0][lane];
 
-    // The loop requests chunk c + NBUF - 1 during chunk c's QK^T, one DMA
-    // every few MFMAs: LDS-DMA is throttled at issue per compute unit, and a
+    // The loop requests chunk c + 2 during chunk c's QK^T (chunks 1 and 2
+    // during chunk 0's), one DMA every few MFMAs: LDS-DMA is throttled at
+    // issue per compute unit, so more chunks in flight only queue up, and a
     // burst of requests would hold the issuing waves back before their MFMAs.
-    // Its row numbers are read a chunk ahead (lane k holds the wave's k-th),
-    // so requesting one only moves it to an SGPR.
+    // Row numbers are read a chunk ahead (lane k holds the wave's k-th), so
+    // requesting one only moves it to an SGPR.
     auto rows_of = [&](int c) {
         const int e0 = lo + c * KC;
         const int e = e0 + (lane % IPW) * NW + wid;
         return list[e < hi ? e : e0];
     };
-    int next_rows = NBUF - 1 < nchunks ? rows_of(NBUF - 1) : 0;
+    int next_rows = 1 < nchunks ? rows_of(1) : 0;   // the chunk requested next
+    int next2_rows = 2 < nchunks ? rows_of(2) : 0;  // chunk 2, during chunk 0
     for (int c = 0; c < nchunks; ++c) {
-        // chunk c has landed once at most `ahead` later chunks are pending
-        wait_vm_ahead<IPW, NBUF - 2>(min(NBUF - 2, nchunks - 1 - c));
+        // chunk c has landed once at most the chunk after it is pending
+        wait_vm_ahead<IPW, 1>(min(1, nchunks - 1 - c));
         __syncthreads();
-        // slot (c + NBUF - 1) % NBUF was last read by chunk c - 1, which every
-        // wave finished before the barrier above
-        const bool do_stage = c + NBUF - 1 < nchunks;
+        // chunk c + 2 goes into slot (c + 2) % NBUF, last read by chunk c - 2,
+        // which every wave finished before the barrier above
+        const int rq = c == 0 ? 1 : c + 2;  // first chunk requested in this QK^T
+        const bool do_stage = rq < nchunks;
+        const bool two = c == 0 && 2 < nchunks;  // chunk 2 as well
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NBUF][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
@@ -676,15 +655,21 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
                     sacc[i & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i % QKP], qf[t][i >> 1],
                                                                              sacc[i & 1][t], 0, 0, 0);
                 if (i + QKP < NQK) ka[i % QKP] = kload(i + QKP);
-                if (do_stage) {  // DMAs k in [i*IPW/NQK, (i+1)*IPW/NQK): spread evenly
+                if (two) {  // 2*IPW DMAs spread evenly: chunk 1's rows, then chunk 2's
+#pragma unroll
+                    for (int k = i * 2 * IPW / NQK; k < (i + 1) * 2 * IPW / NQK; ++k) {
+                        if (k < IPW) dma_row(1, k, __builtin_amdgcn_readlane(next_rows, k));
+                        else dma_row(2, k - IPW, __builtin_amdgcn_readlane(next2_rows, k - IPW));
+                    }
+                } else if (do_stage) {  // DMAs k in [i*IPW/NQK, (i+1)*IPW/NQK): spread evenly
 #pragma unroll
                     for (int k = i * IPW / NQK; k < (i + 1) * IPW / NQK; ++k)
-                        dma_row(c + NBUF - 1, k, __builtin_amdgcn_readlane(next_rows, k));
+                        dma_row(rq, k, __builtin_amdgcn_readlane(next_rows, k));
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (do_stage && c + NBUF < nchunks) next_rows = rows_of(c + NBUF);
+        if (c + 3 < nchunks) next_rows = rows_of(c + 3);
         // the pair adds its two halves (a + b == b + a, so both waves agree)
 #pragma unroll
         for (int t = 0; t < HT; ++t) {
