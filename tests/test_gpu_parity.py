@@ -605,3 +605,23 @@ def test_full_ragged_sampled(ref):
     pick = sorted(set(list(order[:16]) + list(order[-16:]) +
                       list(np.random.default_rng(1).choice(256, 32, replace=False))))
     sampled_check(ref, w, [(int(b), 0) for b in pick], got)
+
+
+def test_full_decode_with_unused_entries_in_every_slice(ref):
+    """The decode batch with unused (-1) and out-of-range (>= N) entries spread
+    through every split's slice, in the launch configuration bench.py times:
+    the rows a fully valid list would put in each split's first chunk are
+    requested before the list is compacted and then corrected, so the result
+    must equal the oracle on the cleaned lists (out-of-range entries skipped)."""
+    w = wl.make("decode")
+    rng = np.random.default_rng(5)
+    lst = w.idxs.copy()
+    lst[rng.random(lst.shape) < 0.15] = -1
+    lst[rng.random(lst.shape) < 0.02] = w.N + 7
+    got = run_gpu(w, 0, idxs=lst)
+    clean = np.where(lst >= w.N, -1, lst).astype(np.int32)
+    exps = []
+    for b in range(w.B):
+        q1, kv1, _ = w.query_slice(b, 0)
+        exps.append(ref(q1, kv1, w.sink, clean[b:b + 1, 0:1], w.scale)[0, 0])
+    assert_close(got[:, 0], np.stack(exps), "decode with unused and out-of-range entries")
