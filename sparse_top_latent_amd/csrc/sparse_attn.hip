@@ -289,13 +289,16 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
             // A split's partial: fp16 rows (11 significant bits) scaled by a
             // power of two per (head, half row) so that |value| < 2^15 never
             // overflows.
+            // inv >= 0 and rounding is monotonic, so max |o| * inv is exactly
+            // max |o * inv|
             float amax = 0.f;
 #pragma unroll
             for (int u = 0; u < DTH; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[t][u][i] * inv));
+                for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[t][u][i]));
             amax = fmaxf(amax, shfl_xor_f(amax, 16));
             amax = fmaxf(amax, shfl_xor_f(amax, 32));
+            amax *= inv;
             int ex = 0;
             if (amax < INFINITY) (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1)
             const int e = ex > 15 ? ex - 15 : 0;
