@@ -322,7 +322,10 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
         }
     }
     __syncthreads();
-    // every LDS read first, then every store (one LDS round trip in all)
+    // every LDS read first, then every store (one LDS round trip in all).
+    // The stores are non-temporal: outputs and split partials are written
+    // once and read once, by a later kernel, so they bypass the caches'
+    // allocation (partials: ~9% off the decode main kernel).
     uint16_t *dst = p.S == 1 ? p.out + (int64_t)qi * p.H * D
                              : p.ws_o + ((int64_t)qi * p.S + s) * p.H * D;
     constexpr int NIT = HWG * C16 / NT;
@@ -338,7 +341,7 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
         const int i = it * NT + tid;
         const int r = i / C16, pos = i % C16;
         if (hbase + r < p.H)
-            *(u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)) = v[it];
+            __builtin_nontemporal_store(v[it], (u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)));
     }
 }
 
@@ -1070,7 +1073,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     u32x4_t v[SB];
 #pragma unroll
     for (int j = 0; j < SB; ++j)
-        v[j] = ok && j < S ? *(const u32x4_t *)(ws_o + (slot0 + (int64_t)j * H) * D + c8)
+        v[j] = ok && j < S ? __builtin_nontemporal_load((const u32x4_t *)(ws_o + (slot0 + (int64_t)j * H) * D + c8))
                            : u32x4_t{0, 0, 0, 0};
     // rotary dims: the (cos, sin) of the lane's four pairs
     const bool rot = ok && c8 >= D - rd;
@@ -1123,7 +1126,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 #pragma unroll
             for (int j = 0; j < SB; ++j)
                 v[j] = ok && j0 + j < S
-                           ? *(const u32x4_t *)(ws_o + (slot0 + (int64_t)(j0 + j) * H) * D + c8)
+                           ? __builtin_nontemporal_load((const u32x4_t *)(ws_o + (slot0 + (int64_t)(j0 + j) * H) * D + c8))
                            : u32x4_t{0, 0, 0, 0};
         }
 #pragma unroll
