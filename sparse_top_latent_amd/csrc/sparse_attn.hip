@@ -203,6 +203,17 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, const LDS_AS void *l
                  : "memory", "m0");
 }
 
+// Same, non-temporal: for rows that one workgroup reads once (the deep-gather
+// kernel's decode-shaped launches), so they do not take cache lines from data
+// that is reused (q, partials on their way to the combine).
+__device__ __forceinline__ void lds_dma16_nt(const void *gptr, const LDS_AS void *lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(gptr), "s"(m0)
+                 : "memory", "m0");
+}
+
 // Same with a wave-uniform row base in SGPRs and a per-lane byte offset
 // (saddr form: no 64-bit per-lane address arithmetic).
 __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff,
@@ -517,9 +528,9 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (k * NW + wid) * RS;
         if (!FP4 || rw < p.W) {
             if (CPR == 64 || lane < CPR)
-                lds_dma16((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8, (LDS_AS void *)dst);
+                lds_dma16_nt((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8, (LDS_AS void *)dst);
         } else if (lane * 16 < p.rec2) {
-            lds_dma16(recb + (int64_t)rw * p.rec2 + lane * 16, (LDS_AS void *)(dst + RS - p.rec2));
+            lds_dma16_nt(recb + (int64_t)rw * p.rec2 + lane * 16, (LDS_AS void *)(dst + RS - p.rec2));
         }
     };
 
