@@ -41,6 +41,13 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int KC = 32;                // rows (list entries) per chunk
+constexpr int DMA_LAG = 6;            // QK^T steps before a group of row DMAs goes out
+
+// The QK^T step that issues group q of ng groups of row DMAs spread evenly
+// over nsteps steps.
+constexpr int dma_step(int q, int ng, int nsteps) {
+    return q * nsteps / ng + DMA_LAG < nsteps ? q * nsteps / ng + DMA_LAG : nsteps - 1;
+}
 constexpr int LIST_CAP = 2048;        // longest index list a workgroup compacts
 constexpr int MAX_SPLITS = 64;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -222,6 +229,47 @@ __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff,
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+}
+
+// Four rows with one M0 write.  The instruction offset is added to both the
+// global and the LDS address, so row j (0..3) lands at lds_base + j*RS +
+// 16*lane when its global address is passed less j*RS.  Writing M0 once per
+// four rows instead of once per row roughly doubles the rate at which a
+// compute unit issues these DMAs (a 640-row-per-workgroup gather over 64
+// workgroups takes 17 us instead of 33).  The addresses less j*RS are never
+// accessed themselves.
+template <int RS>
+__device__ __forceinline__ void lds_dma16x4_nt(const uint8_t *g0, const uint8_t *g1, const uint8_t *g2,
+                                               const uint8_t *g3, const LDS_AS void *lds_base) {
+    static_assert(3 * RS < 4096, "row offsets fit the instruction's offset field");
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %4\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, off nt\n\t"
+                 "global_load_lds_dwordx4 %1, off offset:%5 nt\n\t"
+                 "global_load_lds_dwordx4 %2, off offset:%6 nt\n\t"
+                 "global_load_lds_dwordx4 %3, off offset:%7 nt"
+                 :
+                 : "v"(g0), "v"(g1 - RS), "v"(g2 - 2 * RS), "v"(g3 - 3 * RS), "s"(m0), "n"(RS),
+                   "n"(2 * RS), "n"(3 * RS)
+                 : "memory", "m0");
+}
+
+// Same in the saddr form: wave-uniform row bases in SGPRs, one per-lane byte
+// offset shared by the four rows.
+template <int RS>
+__device__ __forceinline__ void lds_dma16x4_s(const uint8_t *s0, const uint8_t *s1, const uint8_t *s2,
+                                              const uint8_t *s3, uint32_t voff, const LDS_AS void *lds_base) {
+    static_assert(3 * RS < 4096, "row offsets fit the instruction's offset field");
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %2 offset:%6\n\t"
+                 "global_load_lds_dwordx4 %0, %3 offset:%7\n\t"
+                 "global_load_lds_dwordx4 %0, %4 offset:%8"
+                 :
+                 : "v"(voff), "s"(s0), "s"(s1 - RS), "s"(s2 - 2 * RS), "s"(s3 - 3 * RS), "s"(m0),
+                   "n"(RS), "n"(2 * RS), "n"(3 * RS)
                  : "memory", "m0");
 }
 
@@ -494,7 +542,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 
     // Prologue.  Per wave, in issue order: its share of the raw list (LDS-DMA,
     // 4 bytes per lane, into slot 3), its q (ordinary loads straight into the
-    // MFMA B operands: LDS-DMA is throttled at issue per compute unit, and q
+    // MFMA B operands: a compute unit issues LDS-DMA at a limited rate, and q
     // would queue 64 KB ahead of the first rows), then chunk 0 as soon as the
     // list has landed.
     LDS_AS int32_t *raw = (LDS_AS int32_t *)&tile[3][0];
@@ -521,16 +569,35 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     __syncthreads();
 
     // a2: the wave's k-th row of chunk c into ring slot c % NBUF with LDS-DMA.
-    // Each wave instruction moves one row: lane l < D/8 fetches its 16 bytes
-    // and lands at byte 16*l of the row's padded slot (an FP4 record, FP4
-    // build and rows >= W: lanes < rec2/16, at the tail of the slot).
+    // A wave takes IPW consecutive entries of the chunk (its k-th is entry
+    // wid*IPW + k, at that position of the slot), so that four of its rows
+    // sit within reach of one instruction's offset.  Each wave instruction
+    // moves one row: lane l < D/8 fetches its 16 bytes and lands at byte 16*l
+    // of the row's padded slot (an FP4 record, FP4 build and rows >= W: lanes
+    // < rec2/16, at the tail of the slot).
+    static_assert(IPW % 4 == 0, "rows are requested four at a time");
     auto dma_row = [&](int c, int k, int rw) {
-        LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (k * NW + wid) * RS;
+        LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (wid * IPW + k) * RS;
         if (!FP4 || rw < p.W) {
             if (CPR == 64 || lane < CPR)
                 lds_dma16_nt((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8, (LDS_AS void *)dst);
         } else if (lane * 16 < p.rec2) {
             lds_dma16_nt(recb + (int64_t)rw * p.rec2 + lane * 16, (LDS_AS void *)(dst + RS - p.rec2));
+        }
+    };
+    // the wave's rows k0 .. k0+3 of chunk c (bf16 rows: one M0 write)
+    auto dma_quad = [&](int c, int k0, int r0, int r1, int r2, int r3) {
+        if constexpr (FP4) {
+            dma_row(c, k0, r0);
+            dma_row(c, k0 + 1, r1);
+            dma_row(c, k0 + 2, r2);
+            dma_row(c, k0 + 3, r3);
+        } else {
+            LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (wid * IPW + k0) * RS;
+            auto src = [&](int rw) {
+                return (const uint8_t *)((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8);
+            };
+            if (CPR == 64 || lane < CPR) lds_dma16x4_nt<RS>(src(r0), src(r1), src(r2), src(r3), dst);
         }
     };
 
@@ -546,14 +613,21 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         const int slo = (p.K * s) / p.S, shi = (p.K * (s + 1)) / p.S;  // K <= LIST_CAP
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
-            const int e = slo + k * NW + wid;
+            const int e = slo + wid * IPW + k;
             const int v = slo < shi ? raw[e < shi ? e : slo] : -1;
             const int rw = __builtin_amdgcn_readfirstlane(v);
             spec[k] = rw >= 0 && (int64_t)rw < p.N ? rw : -1;
         }
 #pragma unroll
-        for (int k = 0; k < IPW; ++k)
-            if (spec[k] >= 0) dma_row(0, k, spec[k]);
+        for (int k = 0; k < IPW; k += 4) {
+            if ((spec[k] | spec[k + 1] | spec[k + 2] | spec[k + 3]) >= 0) {
+                dma_quad(0, k, spec[k], spec[k + 1], spec[k + 2], spec[k + 3]);
+            } else {
+#pragma unroll
+                for (int j = k; j < k + 4; ++j)
+                    if (spec[j] >= 0) dma_row(0, j, spec[j]);
+            }
+        }
     }
 
     // a1: decode and compact the list, then take this split's slice.
@@ -570,16 +644,10 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         const int e0 = lo + c * KC;
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
-            const int e = e0 + k * NW + wid;
+            const int e = e0 + wid * IPW + k;
             // the row number is wave-uniform: scalar branches, one DMA per row
             row[k] = __builtin_amdgcn_readfirstlane(list[e < hi ? e : e0]);
         }
-    };
-    auto stage = [&](int c) {
-        int row[IPW];
-        chunk_rows(c, row);
-#pragma unroll
-        for (int k = 0; k < IPW; ++k) dma_row(c, k, row[k]);
     };
     if (nchunks > 0) {
         int row[IPW];
@@ -618,15 +686,20 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     const LDS_AS f32x4_t *xpeer = (const LDS_AS f32x4_t *)&xbuf[wid ^ 1][0][lane];
 
     // The loop requests chunk c + 2 during chunk c's QK^T (chunks 1 and 2
-    // during chunk 0's), one DMA every few MFMAs: LDS-DMA is throttled at
-    // issue per compute unit, so more chunks in flight only queue up, and a
-    // burst of requests would hold the issuing waves back before their MFMAs.
-    // Row numbers are read a chunk ahead (lane k holds the wave's k-th), so
-    // requesting one only moves it to an SGPR.
+    // during chunk 0's), a group of four rows between MFMAs: a compute unit
+    // issues LDS-DMA at a limited rate, so more chunks in flight only queue
+    // up, and a burst of requests would hold the issuing waves back before
+    // their MFMAs.  Row numbers are read a chunk ahead (lane k holds the
+    // wave's k-th), so requesting one only moves it to an SGPR.
     auto rows_of = [&](int c) {
         const int e0 = lo + c * KC;
-        const int e = e0 + (lane % IPW) * NW + wid;
+        const int e = e0 + wid * IPW + lane % IPW;
         return list[e < hi ? e : e0];
+    };
+    // the wave's rows 4q .. 4q+3 of chunk cc, from the lanes of `rows`
+    auto quad_from = [&](int cc, int q, int rows) {
+        dma_quad(cc, 4 * q, __builtin_amdgcn_readlane(rows, 4 * q), __builtin_amdgcn_readlane(rows, 4 * q + 1),
+                 __builtin_amdgcn_readlane(rows, 4 * q + 2), __builtin_amdgcn_readlane(rows, 4 * q + 3));
     };
     int next_rows = 1 < nchunks ? rows_of(1) : 0;   // the chunk requested next
     int next2_rows = 2 < nchunks ? rows_of(2) : 0;  // chunk 2, during chunk 0
@@ -672,16 +745,20 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
                     sacc[i & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i % QKP], qf[t][i >> 1],
                                                                              sacc[i & 1][t], 0, 0, 0);
                 if (i + QKP < NQK) ka[i % QKP] = kload(i + QKP);
-                if (two) {  // 2*IPW DMAs spread evenly: chunk 1's rows, then chunk 2's
+                // groups of four rows, spread evenly (dma_step)
+                if (two) {  // chunk 1's groups, then chunk 2's
+                    constexpr int NG = 2 * IPW / 4;
 #pragma unroll
-                    for (int k = i * 2 * IPW / NQK; k < (i + 1) * 2 * IPW / NQK; ++k) {
-                        if (k < IPW) dma_row(1, k, __builtin_amdgcn_readlane(next_rows, k));
-                        else dma_row(2, k - IPW, __builtin_amdgcn_readlane(next2_rows, k - IPW));
-                    }
-                } else if (do_stage) {  // DMAs k in [i*IPW/NQK, (i+1)*IPW/NQK): spread evenly
+                    for (int q = 0; q < NG; ++q)
+                        if (i == dma_step(q, NG, NQK)) {
+                            if (q < NG / 2) quad_from(1, q, next_rows);
+                            else quad_from(2, q - NG / 2, next2_rows);
+                        }
+                } else if (do_stage) {
+                    constexpr int NG = IPW / 4;
 #pragma unroll
-                    for (int k = i * IPW / NQK; k < (i + 1) * IPW / NQK; ++k)
-                        dma_row(rq, k, __builtin_amdgcn_readlane(next_rows, k));
+                    for (int q = 0; q < NG; ++q)
+                        if (i == dma_step(q, NG, NQK)) quad_from(rq, q, next_rows);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -854,20 +931,22 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     const int nchunks = (hi - lo + KC - 1) / KC;
 
     // a2: chunk c (KC rows) into ring slot c % NB, one row per DMA
-    // instruction (row r = k*NW + wid for the wave's k-th); tail slots repeat
-    // the chunk's first row (masked below).  rows_of reads the chunk's row
-    // numbers one chunk ahead (lane k holds the k-th), so a stage only moves
-    // them to SGPRs and issues the DMAs.
+    // instruction; the wave's k-th is entry wid*IPW + k, at that position of
+    // the slot, so four of its rows sit within reach of one instruction's
+    // offset.  Tail slots repeat the chunk's first row (masked below).
+    // rows_of reads the chunk's row numbers one chunk ahead (lane k holds the
+    // k-th), so a stage only moves them to SGPRs and issues the DMAs.
+    static_assert(IPW % 4 == 0, "rows are requested four at a time");
     auto rows_of = [&](int c) {
         const int e0 = lo + c * KC;
-        const int e = e0 + (lane % IPW) * NW + wid;
+        const int e = e0 + wid * IPW + lane % IPW;
         return list[e < hi ? e : e0];
     };
     // this wave's k-th row of chunk c: a bf16 row, or (FP4 build, rows >= W)
     // a record landing at the tail of the row's slot
     auto stage_one = [&](int c, int rows, int k) {
         const int row = __builtin_amdgcn_readlane(rows, k);
-        LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NB][0] + (k * NW + wid) * RS;
+        LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NB][0] + (wid * IPW + k) * RS;
         if (!FP4 || row < p.W) {
             const uint16_t *src = (row < p.W ? kva : kvb2) + (int64_t)row * D;
             if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, dst);
@@ -875,9 +954,24 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
             lds_dma16_s(recb + (int64_t)row * p.rec2, lane * 16, dst + RS - p.rec2);
         }
     };
+    // rows 4q .. 4q+3 (bf16 rows: one M0 write)
+    auto stage_quad = [&](int c, int rows, int q) {
+        if constexpr (FP4) {
+#pragma unroll
+            for (int k = 4 * q; k < 4 * q + 4; ++k) stage_one(c, rows, k);
+        } else {
+            auto src = [&](int k) {
+                const int row = __builtin_amdgcn_readlane(rows, k);
+                return (const uint8_t *)((row < p.W ? kva : kvb2) + (int64_t)row * D);
+            };
+            LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NB][0] + (wid * IPW + 4 * q) * RS;
+            if (CPR == 64 || lane < CPR)
+                lds_dma16x4_s<RS>(src(4 * q), src(4 * q + 1), src(4 * q + 2), src(4 * q + 3), lane * 16, dst);
+        }
+    };
     auto stage = [&](int c, int rows) {
 #pragma unroll
-        for (int k = 0; k < IPW; ++k) stage_one(c, rows, k);
+        for (int q = 0; q < IPW / 4; ++q) stage_quad(c, rows, q);
     };
     int next_rows = 0;
     if (nchunks > 0) stage(0, rows_of(0));
@@ -939,10 +1033,11 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
                 sacc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i % QKP], qf[i >> 1],
                                                                       sacc[i & 1], 0, 0, 0);
                 if (i + QKP < NQK) ka[i % QKP] = kload(i + QKP);
-                if (do_stage) {  // DMAs k in [i*IPW/NQK, (i+1)*IPW/NQK): spread evenly
+                if (do_stage) {  // groups of four rows, spread evenly (dma_step)
+                    constexpr int NG = IPW / 4;
 #pragma unroll
-                    for (int k = i * IPW / NQK; k < (i + 1) * IPW / NQK; ++k)
-                        stage_one(c + 1, next_rows, k);
+                    for (int q = 0; q < NG; ++q)
+                        if (i == dma_step(q, NG, NQK)) stage_quad(c + 1, next_rows, q);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1521,11 +1616,12 @@ WsLayout ws_layout(const sa_dims *d, int S) {
 
 // Split count for launches with fewer units than compute units.  A split
 // shortens every workgroup's share of the list, but its partials cost a
-// combine kernel worth about four 32-row chunks of the attention kernel
-// (measured on MI355X at 64 heads: ~1.3 us per chunk, ~5.5 us per combine).
-// S minimises rounds(S) * K/(32 S) + (S > 1 ? 4 : 0), where rounds(S) is the
-// number of waves of workgroups over the compute units, among S up to
-// ceil(CUs / units) and K/64.
+// combine kernel worth about four 32-row chunks of the attention kernel plus
+// one per split (fitted on MI355X at 64 heads and 640 entries: ~1.2 us per
+// chunk, ~5.5 us per combine, and the step at 32 and 64 queries over S = 2
+// to 16).  S minimises rounds(S) * K/(32 S) + (S > 1 ? 4 + S : 0), where
+// rounds(S) is the number of waves of workgroups over the compute units,
+// among S up to ceil(CUs / units) and K/64.
 int plan_splits(const sa_dims *d) {
     const int cus = device_cu_count();
     if (cus < 0) return -SA_ERR_HIP;
@@ -1539,7 +1635,7 @@ int plan_splits(const sa_dims *d) {
     double best_cost = d->K / 32.0;
     for (int64_t S = 2; S <= smax; ++S) {
         const int64_t rounds = (units * S + cus - 1) / cus;
-        const double cost = (double)rounds * d->K / (32.0 * S) + 4.0;
+        const double cost = (double)rounds * d->K / (32.0 * S) + 4.0 + (double)S;
         if (cost < best_cost) {
             best_cost = cost;
             best = (int)S;
