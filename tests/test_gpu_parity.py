@@ -244,6 +244,29 @@ def test_plan_kernel_names_the_dispatch():
     assert api.plan_kernel(q, kv, idx, 0) == "attn_fwd_mq_kernel<512,2,false>"
 
 
+# The split counts the planner gives the benchmark shapes on a 256-CU device
+# (H=64, D=512; the planner reads only B, T, H and K): the counts the split
+# sweeps measured fastest.  Other devices skip.
+@pytest.mark.parametrize("B,T,K,expected", [
+    (64, 1, 640, 4),     # decode
+    (32, 1, 640, 4),     # long context
+    (64, 1, 128, 1),     # sliding window only
+    (256, 1, 640, 1),    # ragged batch
+    (1, 4096, 640, 1),   # prefill
+    (1, 1, 640, 4),      # a single query: more splits cost more in the combine
+    (1, 1, 128, 1),      # a single short query
+    (8, 1, 32, 1),       # shorter than two chunks
+])
+def test_planned_split_counts(B, T, K, expected):
+    import ctypes
+    torch = torch_mod()
+    from sparse_top_latent_amd import _lib
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("split counts pinned for a 256-CU device")
+    d = _lib.SaDims(B, T, 64, 512, 8320, K)
+    assert _lib.lib().sparse_attn_plan_splits(ctypes.byref(d)) == expected
+
+
 def test_many_query_splits_stress_and_long_lists(ref):
     T = many_query_T()
     w = wl.make_random(210, 2, T, 64, 512, 120, 40, p_unused=0.2)
