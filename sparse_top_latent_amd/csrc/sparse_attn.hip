@@ -238,7 +238,11 @@ __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff,
 // four rows instead of once per row roughly doubles the rate at which a
 // compute unit issues these DMAs (a 640-row-per-workgroup gather over 64
 // workgroups takes 17 us instead of 33).  The addresses less j*RS are never
-// accessed themselves.
+// accessed themselves; they are formed as integers (they may lie before the
+// allocation).
+__device__ __forceinline__ uint64_t addr_less(const uint8_t *p, int bytes) {
+    return (uint64_t)(uintptr_t)p - (uint64_t)bytes;
+}
 template <int RS>
 __device__ __forceinline__ void lds_dma16x4_nt(const uint8_t *g0, const uint8_t *g1, const uint8_t *g2,
                                                const uint8_t *g3, const LDS_AS void *lds_base) {
@@ -250,8 +254,8 @@ __device__ __forceinline__ void lds_dma16x4_nt(const uint8_t *g0, const uint8_t 
                  "global_load_lds_dwordx4 %2, off offset:%6 nt\n\t"
                  "global_load_lds_dwordx4 %3, off offset:%7 nt"
                  :
-                 : "v"(g0), "v"(g1 - RS), "v"(g2 - 2 * RS), "v"(g3 - 3 * RS), "s"(m0), "n"(RS),
-                   "n"(2 * RS), "n"(3 * RS)
+                 : "v"(g0), "v"(addr_less(g1, RS)), "v"(addr_less(g2, 2 * RS)), "v"(addr_less(g3, 3 * RS)),
+                   "s"(m0), "n"(RS), "n"(2 * RS), "n"(3 * RS)
                  : "memory", "m0");
 }
 
@@ -268,8 +272,8 @@ __device__ __forceinline__ void lds_dma16x4_s(const uint8_t *s0, const uint8_t *
                  "global_load_lds_dwordx4 %0, %3 offset:%7\n\t"
                  "global_load_lds_dwordx4 %0, %4 offset:%8"
                  :
-                 : "v"(voff), "s"(s0), "s"(s1 - RS), "s"(s2 - 2 * RS), "s"(s3 - 3 * RS), "s"(m0),
-                   "n"(RS), "n"(2 * RS), "n"(3 * RS)
+                 : "v"(voff), "s"(s0), "s"(addr_less(s1, RS)), "s"(addr_less(s2, 2 * RS)),
+                   "s"(addr_less(s3, 3 * RS)), "s"(m0), "n"(RS), "n"(2 * RS), "n"(3 * RS)
                  : "memory", "m0");
 }
 
