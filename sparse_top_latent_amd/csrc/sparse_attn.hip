@@ -1601,6 +1601,28 @@ bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) =
 
 int64_t queries(const sa_dims *d) { return (int64_t)d->B * d->T; }
 
+// The shape a call with S splits launches.  Above 32 heads a deep-gather
+// workgroup serves 64 heads; when the workgroups of 32 heads (two wave pairs)
+// would still fit the compute units in one round, it serves 32 instead:
+// twice the workgroups on a launch that would leave half of the compute units
+// idle, each row read by two of them (the second read mostly from L2: both
+// sit on one XCD).  Measured at H=64, 640 entries: 32 queries at S=4 take
+// 18.4 us per step instead of 20.1, 64 window-only lists at S=1 12.6 instead
+// of 13.3; where 64-head workgroups already fill the device (64 queries at
+// S=4, 256 queries at S=1) they stay (24.8 and 65 us otherwise, against 23.4
+// and 41).  The split count is planned with the 64-head shape.
+WgShape shape_for(const sa_dims *d, int S) {
+    const WgShape base = shape_for(d->H);
+    if (base.nhq != 4) return base;
+    const int cus = device_cu_count();
+    const int64_t narrow_units = queries(d) * ((d->H + 31) / 32) * S;
+    return cus > 0 && narrow_units <= cus ? WgShape{2, 1} : base;
+}
+int head_groups(const sa_dims *d, int S) {
+    const int h = shape_for(d, S).heads();
+    return (d->H + h - 1) / h;
+}
+
 struct WsLayout {
     size_t o_off, m_off, l_off, x_off, bytes;
 };
@@ -1662,7 +1684,11 @@ hipError_t launch_fwd(const FwdParams &p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_fwd_d(WgShape w, const FwdParams &p, hipStream_t stream) {
-    if (w.ht == 1) return w.nhq == 4 ? launch_fwd<D, 4, 1>(p, stream) : launch_fwd<D, 1, 1>(p, stream);
+    if (w.ht == 1) {
+        if (w.nhq == 4) return launch_fwd<D, 4, 1>(p, stream);
+        if (w.nhq == 2) return launch_fwd<D, 2, 1>(p, stream);
+        return launch_fwd<D, 1, 1>(p, stream);
+    }
     return launch_fwd<D, 1, 2>(p, stream);
 }
 
@@ -1742,7 +1768,7 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
     p.H = d->H;
     p.K = d->K;
     p.S = S;
-    p.HG = head_groups(d->H);
+    p.HG = head_groups(d, S);
     const int64_t units = queries(d) * p.HG * S;
     p.units = (int32_t)units;
     // blocks of up to 64 queries' units per XCD turn (see unit_of)
@@ -1775,7 +1801,8 @@ bool use_mq(const FwdParams &p, int H) {
     return H > 16 && cus > 0 && (int64_t)p.units >= 2 * (int64_t)cus;
 }
 
-hipError_t run_fwd(const FwdParams &p, int D, int H, hipStream_t stream) {
+hipError_t run_fwd(const FwdParams &p, const sa_dims *d, hipStream_t stream) {
+    const int D = d->D, H = d->H;
     if (use_mq(p, H)) {
         const bool two = H > 32;
         switch (D) {
@@ -1784,7 +1811,7 @@ hipError_t run_fwd(const FwdParams &p, int D, int H, hipStream_t stream) {
             default: return two ? launch_mq<512, 2>(p, stream) : launch_mq<512, 1>(p, stream);
         }
     }
-    const WgShape w = shape_for(H);
+    const WgShape w = shape_for(d, p.S);
     switch (D) {
         case 128: return launch_fwd_d<128>(w, p, stream);
         case 256: return launch_fwd_d<256>(w, p, stream);
@@ -1795,7 +1822,7 @@ hipError_t run_fwd(const FwdParams &p, int D, int H, hipStream_t stream) {
 // unit and workgroup numbers (including the spare workgroups of the last
 // XCD turn, at most 8 blocks of 64 queries' units) stay below 2^31
 bool units_fit(const sa_dims *d, int S) {
-    const int64_t per_q = (int64_t)head_groups(d->H) * S;
+    const int64_t per_q = (int64_t)head_groups(d, S) * S;
     return queries(d) * per_q + 512 * per_q <= (int64_t)0x7FFFFFF0;
 }
 
@@ -1841,7 +1868,7 @@ int sparse_attn_fwd_rope(const void *q, const void *kv, const float *sink, const
     FwdParams p = make_params(q, kv, sink, idxs, scale, out, d, S, workspace);
     p.rope = rd > 0 ? freqs : nullptr;
     p.rd = rd;
-    if (run_fwd(p, d->D, d->H, stream) != hipSuccess) return SA_ERR_HIP;
+    if (run_fwd(p, d, stream) != hipSuccess) return SA_ERR_HIP;
     if (S > 1 && launch_combine(d, S, sink, out, workspace, ws_layout(d, S), stream, p.rope,
                                 rd) != hipSuccess)
         return SA_ERR_HIP;
@@ -1879,7 +1906,7 @@ int fwd_two_source(const void *q, const void *kv_win, int32_t win_rows, const vo
     p.rows_a = win_rows;
     p.rows_b = cmp_rows;
     p.rec2 = rec;
-    if (run_fwd(p, d->D, d->H, stream) != hipSuccess) return SA_ERR_HIP;
+    if (run_fwd(p, d, stream) != hipSuccess) return SA_ERR_HIP;
     if (S > 1 && launch_combine(d, S, sink, out, workspace, ws_layout(d, S), stream) != hipSuccess)
         return SA_ERR_HIP;
     return SA_OK;
@@ -1924,7 +1951,7 @@ int sparse_attn_fwd_partial(const void *q, const void *kv, const int32_t *idxs, 
     if (queries(d) == 0) return SA_OK;
     if (!units_fit(d, S)) return SA_ERR_SHAPE;
     const FwdParams p = make_params(q, kv, nullptr, idxs, scale, nullptr, d, S, workspace);
-    return run_fwd(p, d->D, d->H, stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+    return run_fwd(p, d, stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
 int sparse_attn_fwd_combine(const float *sink, void *out, const sa_dims *d, int32_t num_splits,
@@ -1966,7 +1993,7 @@ const char *sparse_attn_plan_kernel(const sa_dims *d, int32_t num_splits) {
         if (S < 0) return nullptr;
     }
     FwdParams p{};
-    p.units = (int32_t)(queries(d) * head_groups(d->H) * S);
+    p.units = (int32_t)(queries(d) * head_groups(d, S) * S);
     if (use_mq(p, d->H)) {
         const bool two = d->H > 32;
         switch (d->D) {
@@ -1975,13 +2002,16 @@ const char *sparse_attn_plan_kernel(const sa_dims *d, int32_t num_splits) {
             default: return two ? "attn_fwd_mq_kernel<512,2,false>" : "attn_fwd_mq_kernel<512,1,false>";
         }
     }
-    const WgShape w = shape_for(d->H);
-    static const char *names[3][3] = {
-        {"attn_fwd_kernel<128,4,1,false>", "attn_fwd_kernel<128,1,2,false>", "attn_fwd_kernel<128,1,1,false>"},
-        {"attn_fwd_kernel<256,4,1,false>", "attn_fwd_kernel<256,1,2,false>", "attn_fwd_kernel<256,1,1,false>"},
-        {"attn_fwd_kernel<512,4,1,false>", "attn_fwd_kernel<512,1,2,false>", "attn_fwd_kernel<512,1,1,false>"}};
+    const WgShape w = shape_for(d, S);
+    static const char *names[3][4] = {
+        {"attn_fwd_kernel<128,4,1,false>", "attn_fwd_kernel<128,1,2,false>", "attn_fwd_kernel<128,1,1,false>",
+         "attn_fwd_kernel<128,2,1,false>"},
+        {"attn_fwd_kernel<256,4,1,false>", "attn_fwd_kernel<256,1,2,false>", "attn_fwd_kernel<256,1,1,false>",
+         "attn_fwd_kernel<256,2,1,false>"},
+        {"attn_fwd_kernel<512,4,1,false>", "attn_fwd_kernel<512,1,2,false>", "attn_fwd_kernel<512,1,1,false>",
+         "attn_fwd_kernel<512,2,1,false>"}};
     const int di = d->D == 128 ? 0 : d->D == 256 ? 1 : 2;
-    const int wi = w.ht == 1 ? (w.nhq == 4 ? 0 : 2) : 1;
+    const int wi = w.ht == 1 ? (w.nhq == 4 ? 0 : w.nhq == 2 ? 3 : 2) : 1;
     return names[di][wi];
 }
 

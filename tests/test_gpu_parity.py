@@ -234,14 +234,35 @@ def test_many_query_path(ref, H, D):
 
 
 def test_plan_kernel_names_the_dispatch():
+    import ctypes
     torch = torch_mod()
-    from sparse_top_latent_amd import api
+    from sparse_top_latent_amd import api, _lib
     w = wl.make_decode(B=4)
     q, kv, _, idx = to_dev(w)
-    assert api.plan_kernel(q, kv, idx, 4) == "attn_fwd_kernel<512,4,1,false>"
+    # few workgroups: 32 heads per workgroup (two of them per query and split)
+    assert api.plan_kernel(q, kv, idx, 4) == "attn_fwd_kernel<512,2,1,false>"
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        # 64 queries x 4 splits fill the device with 64-head workgroups
+        d = _lib.SaDims(64, 1, 64, 512, 8320, 640)
+        name = _lib.lib().sparse_attn_plan_kernel(ctypes.byref(d), 4)
+        assert name.decode() == "attn_fwd_kernel<512,4,1,false>"
     wm = wl.make_random(212, 2, many_query_T(), 64, 512, 60, 20)
     q, kv, _, idx = to_dev(wm)
     assert api.plan_kernel(q, kv, idx, 0) == "attn_fwd_mq_kernel<512,2,false>"
+
+
+@pytest.mark.parametrize("S", [2, 3])
+def test_sixty_four_head_workgroups(ref, S):
+    # 80 queries: at 2 or 3 splits the 32-head workgroups would not fit 256
+    # compute units in one round, so the 64-head shape runs (on such a
+    # device); K=173 with ~30% unused spans several chunks and a ragged tail
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    w = wl.make_random(300 + S, 4, 20, 64, 512, 300, 173, p_unused=0.3)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        q, kv, _, idx = to_dev(w)
+        assert api.plan_kernel(q, kv, idx, S) == "attn_fwd_kernel<512,4,1,false>"
+    check(ref, w, S, what=f"64-head workgroups S={S}")
 
 
 # The split counts the planner gives the benchmark shapes on a 256-CU device
