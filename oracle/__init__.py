@@ -10,6 +10,12 @@ from it.
 ``build()`` compiles the C source with gcc (-O2, OpenMP, no fast-math);
 ``sparse_attn_ref`` calls it through ctypes on numpy arrays.
 
+Two readings where the pages are silent can be flipped: ``sink_scaled=True``
+multiplies the sink logit by the softmax scale, and ``dedup=True`` counts a
+repeated index once (the GLM index mask's reading) instead of once per
+occurrence.  The defaults are the readings the GPU library implements; each
+variant is pinned against its own brute force in the tests.
+
 Parity unpinned: the pair layout of ``rotate_back`` (the pages call
 apply_rotary_emb on the output's rotary dims with inverse=True but do not
 show its body; the reading taken is DeepSeek's complex convention, consecutive
@@ -47,6 +53,10 @@ def _bind(path):
     lib.oracle_sparse_attn_f64.argtypes = [P, P, P, P, ctypes.c_float,
                                            I64, I64, I64, I64, I64, I64, P, P, P]
     lib.oracle_sparse_attn_f64.restype = ctypes.c_int
+    lib.oracle_sparse_attn_f64_flags.argtypes = [P, P, P, P, ctypes.c_float,
+                                                 I64, I64, I64, I64, I64, I64, ctypes.c_int,
+                                                 P, P, P]
+    lib.oracle_sparse_attn_f64_flags.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -70,8 +80,13 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def sparse_attn_ref(q_bits, kv_bits, sink, idxs, scale, *, weights: bool = False):
-    return _call(_load(), q_bits, kv_bits, sink, idxs, scale, weights)
+SINK_SCALED = 1   # flag values of the C entry point
+DEDUP = 2
+
+
+def sparse_attn_ref(q_bits, kv_bits, sink, idxs, scale, *, weights: bool = False,
+                    sink_scaled: bool = False, dedup: bool = False):
+    return _call(_load(), q_bits, kv_bits, sink, idxs, scale, weights, sink_scaled, dedup)
 
 
 def sparse_attn_2src_ref(q_bits, win_bits, cmp_bits, W, N, sink, idxs, scale):
@@ -204,12 +219,13 @@ def ref_from_library(path):
     (the tests use it to run the pins against planted mistakes)."""
     lib = _bind(path)
 
-    def fn(q_bits, kv_bits, sink, idxs, scale, *, weights: bool = False):
-        return _call(lib, q_bits, kv_bits, sink, idxs, scale, weights)
+    def fn(q_bits, kv_bits, sink, idxs, scale, *, weights: bool = False,
+           sink_scaled: bool = False, dedup: bool = False):
+        return _call(lib, q_bits, kv_bits, sink, idxs, scale, weights, sink_scaled, dedup)
     return fn
 
 
-def _call(lib, q_bits, kv_bits, sink, idxs, scale, weights):
+def _call(lib, q_bits, kv_bits, sink, idxs, scale, weights, sink_scaled=False, dedup=False):
     """fp64 sparse attention with a sink.
 
     q_bits  : uint16 bf16 bit patterns [B, T, H, D]
@@ -217,6 +233,7 @@ def _call(lib, q_bits, kv_bits, sink, idxs, scale, weights):
     sink    : float32 [H] or None (no sink)
     idxs    : int32 [B, T, K]; negative entries are unused
     scale   : Python float, rounded to float32 as the GPU boundary receives it
+    sink_scaled, dedup : the alternative readings (see the module docstring)
     Returns out [B, T, H, D] float64, plus (w [B,T,H,K], w_sink [B,T,H]) when
     ``weights`` is true.  Raises ValueError on an index >= N.
     """
@@ -235,9 +252,10 @@ def _call(lib, q_bits, kv_bits, sink, idxs, scale, weights):
     out = np.zeros((B, T, H, D), dtype=np.float64)
     w = np.zeros((B, T, H, K), dtype=np.float64) if weights else None
     ws = np.zeros((B, T, H), dtype=np.float64) if weights else None
-    rc = lib.oracle_sparse_attn_f64(
+    flags = (SINK_SCALED if sink_scaled else 0) | (DEDUP if dedup else 0)
+    rc = lib.oracle_sparse_attn_f64_flags(
         _ptr(q_bits), _ptr(kv_bits), _ptr(sink), _ptr(idxs), ctypes.c_float(scale),
-        B, T, H, D, N, K, _ptr(out), _ptr(w), _ptr(ws))
+        B, T, H, D, N, K, flags, _ptr(out), _ptr(w), _ptr(ws))
     if rc == 1:
         raise ValueError("index list holds an entry >= N")
     if rc != 0:

@@ -26,10 +26,14 @@
  * notes of the repository):
  *  - any negative index means "unused slot" and contributes nothing;
  *  - the sink is a logit in the already-scaled score domain: it adds exp(sink)
- *    to the softmax denominator and has a zero value row (parity unpinned: no
- *    page prints a value that fixes whether the sink is scaled);
- *  - a repeated index counts once per occurrence, as a gather does (parity
- *    unpinned for repeated indices: the GLM mask would count it once);
+ *    to the softmax denominator and has a zero value row.  No page prints a
+ *    value that fixes whether the sink is multiplied by the softmax scale, so
+ *    the other reading (exp(scale * sink)) is selectable (flag ORACLE_SINK_SCALED)
+ *    and each reading is pinned against its own brute force;
+ *  - a repeated index counts once per occurrence, as a gather does.  The GLM
+ *    index mask (a scatter of the selection into a boolean mask) would count it
+ *    once; that reading is selectable too (flag ORACLE_DEDUP: an entry whose
+ *    index already appeared earlier in the same list is skipped);
  *  - with no valid index and no sink the output is zero, never NaN;
  *  - an index >= N breaks the contract: the oracle returns an error.
  *
@@ -67,6 +71,7 @@ int oracle_num_threads(void)
 }
 
 /*
+ * flags : 0 for the default readings, or ORACLE_SINK_SCALED | ORACLE_DEDUP
  * q     : bf16 bits [B, T, H, D]
  * kv    : bf16 bits [B, N, D]
  * sink  : float32 [H], or NULL for "no sink"
@@ -78,10 +83,13 @@ int oracle_num_threads(void)
  * Returns 0, or 1 when some index is >= N (outputs are then unspecified),
  * or 2 on a bad dimension.
  */
-int oracle_sparse_attn_f64(const uint16_t *q, const uint16_t *kv, const float *sink,
-                           const int32_t *idxs, float scale, int64_t B, int64_t T,
-                           int64_t H, int64_t D, int64_t N, int64_t K, double *out,
-                           double *w, double *wsink)
+#define ORACLE_SINK_SCALED 1
+#define ORACLE_DEDUP 2
+
+int oracle_sparse_attn_f64_flags(const uint16_t *q, const uint16_t *kv, const float *sink,
+                                 const int32_t *idxs, float scale, int64_t B, int64_t T,
+                                 int64_t H, int64_t D, int64_t N, int64_t K, int flags,
+                                 double *out, double *w, double *wsink)
 {
     if (B < 0 || T < 0 || H <= 0 || D <= 0 || N < 0 || K < 0)
         return 2;
@@ -96,21 +104,32 @@ int oracle_sparse_attn_f64(const uint16_t *q, const uint16_t *kv, const float *s
         const uint16_t *kvb = kv + b * N * D;
         double *s = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
         double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        char *use = (char *)malloc((size_t)(K > 0 ? K : 1));
 
         for (int64_t k = 0; k < K; ++k)
             if (list[k] >= N)
                 bad = 1;
+        /* which entries take part: the valid ones, and with ORACLE_DEDUP only
+         * the first occurrence of each index */
+        for (int64_t k = 0; k < K; ++k) {
+            use[k] = list[k] >= 0;
+            if (use[k] && (flags & ORACLE_DEDUP))
+                for (int64_t e = 0; e < k; ++e)
+                    if (list[e] == list[k])
+                        use[k] = 0;
+        }
 
         for (int64_t h = 0; h < H && !bad; ++h) {
             const uint16_t *qh = q + (qi * H + h) * D;
             double *oh = out + (qi * H + h) * D;
 
             /* pass 1: scores of the valid entries and their maximum, sink included */
-            const double z = sink ? (double)sink[h] : -INFINITY;
+            const double zraw = sink ? (double)sink[h] : -INFINITY;
+            const double z = (flags & ORACLE_SINK_SCALED) ? sc * zraw : zraw;
             double m = z;
             for (int64_t k = 0; k < K; ++k) {
                 const int32_t j = list[k];
-                if (j < 0)
+                if (!use[k])
                     continue;
                 double dot = 0.0;
                 for (int64_t d = 0; d < D; ++d)
@@ -135,7 +154,7 @@ int oracle_sparse_attn_f64(const uint16_t *q, const uint16_t *kv, const float *s
             const double wz = sink ? exp(z - m) : 0.0;
             double L = wz;
             for (int64_t k = 0; k < K; ++k) {
-                if (list[k] < 0)
+                if (!use[k])
                     continue;
                 s[k] = exp(s[k] - m);
                 L += s[k];
@@ -146,7 +165,7 @@ int oracle_sparse_attn_f64(const uint16_t *q, const uint16_t *kv, const float *s
                 acc[d] = 0.0;
             for (int64_t k = 0; k < K; ++k) {
                 const int32_t j = list[k];
-                if (j < 0)
+                if (!use[k])
                     continue;
                 for (int64_t d = 0; d < D; ++d)
                     acc[d] += s[k] * widen_bf16(kvb[(int64_t)j * D + d]);
@@ -156,12 +175,23 @@ int oracle_sparse_attn_f64(const uint16_t *q, const uint16_t *kv, const float *s
 
             if (w)
                 for (int64_t k = 0; k < K; ++k)
-                    w[(qi * H + h) * K + k] = list[k] < 0 ? 0.0 : s[k] / L;
+                    w[(qi * H + h) * K + k] = use[k] ? s[k] / L : 0.0;
             if (wsink)
                 wsink[qi * H + h] = wz / L;
         }
         free(s);
         free(acc);
+        free(use);
     }
     return bad ? 1 : 0;
+}
+
+/* The default readings (sink not scaled, every occurrence counts). */
+int oracle_sparse_attn_f64(const uint16_t *q, const uint16_t *kv, const float *sink,
+                           const int32_t *idxs, float scale, int64_t B, int64_t T,
+                           int64_t H, int64_t D, int64_t N, int64_t K, double *out,
+                           double *w, double *wsink)
+{
+    return oracle_sparse_attn_f64_flags(q, kv, sink, idxs, scale, B, T, H, D, N, K, 0, out, w,
+                                        wsink);
 }

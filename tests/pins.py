@@ -16,7 +16,16 @@ definitions, not from the oracle:
     zero;
   * torch's scaled_dot_product_attention in float64, with every row valid and
     the sink folded in as an extra key (an extra feature equal to sink/scale
-    against a query feature of 1) whose value row is zero.
+    against a query feature of 1) whose value row is zero;
+  * gathered dense attention: the listed rows gathered entry by entry (a
+    repeated index gives a repeated key and value), a dense softmax over them
+    plus the sink column, times the gathered values.  With repeats this counts
+    an index once per occurrence, where the index mask above counts it once;
+    the two brute forces pin the two readings of repeated indices.
+
+The sink enters every brute force as a logit column.  The default reading
+takes the sink as it is; the alternative (the sink multiplied by the softmax
+scale) is pinned by giving the brute forces the column scale * sink.
 """
 from __future__ import annotations
 
@@ -58,6 +67,28 @@ def dense_masked(q_bits, kv_bits, sink, idxs, scale):
                     continue                               # nothing to attend to: zero
                 p = scipy.special.softmax(full[h])
                 out[b, t, h] = p[:N] @ V
+    return out
+
+
+def gathered_dense(q_bits, kv_bits, sink_logit, idxs, scale):
+    """Dense softmax over the rows gathered entry by entry (repeats included),
+    plus the sink logit column with a zero value row."""
+    q = bf16_bits_to_f32(q_bits).astype(np.float64)
+    kv = bf16_bits_to_f32(kv_bits).astype(np.float64)
+    B, T, H, D = q.shape
+    sc = float(np.float32(scale))
+    out = np.zeros((B, T, H, D))
+    for b in range(B):
+        for t in range(T):
+            lst = idxs[b, t]
+            G = kv[b, lst[lst >= 0]]                       # [n, D], repeats kept
+            for h in range(H):
+                z = -np.inf if sink_logit is None else float(sink_logit[h])
+                logits = np.concatenate([sc * (G @ q[b, t, h]), [z]])
+                if np.all(np.isneginf(logits)):
+                    continue
+                p = scipy.special.softmax(logits)
+                out[b, t, h] = p[:-1] @ G
     return out
 
 
@@ -255,9 +286,64 @@ def check_closed_forms(ref):
     return None
 
 
+def check_repeated_index_readings(ref):
+    """Lists with repeated indices: by default each occurrence counts (the
+    gathered brute force); with dedup=True an index counts once (the index-mask
+    brute force).  The case is chosen so that the two readings differ."""
+    w = make_random(35, 2, 3, 4, 16, 6, 10, p_unused=0.2, allow_repeats=True)
+    kv = _kv(w)
+    sc = float(np.float32(w.scale))
+    for sink in (w.sink, None):
+        per_occ = gathered_dense(w.q, kv, sink, w.idxs, w.scale)
+        once = dense_masked(w.q, kv, sink, w.idxs, w.scale)
+        if not _err(per_occ, once) > 1e-3:
+            return "test case does not separate the two readings"
+        e = _err(ref(w.q, kv, sink, w.idxs, w.scale), per_occ)
+        if not e <= TOL:
+            return f"repeated indices (per occurrence) off by {e:.3g}"
+        e = _err(ref(w.q, kv, sink, w.idxs, w.scale, dedup=True), once)
+        if not e <= TOL:
+            return f"repeated indices (dedup) off by {e:.3g}"
+        # both alternative readings at once
+        z = None if sink is None else sc * np.asarray(sink, np.float64)
+        e = _err(ref(w.q, kv, sink, w.idxs, w.scale, dedup=True, sink_scaled=True),
+                 dense_masked(w.q, kv, z, w.idxs, w.scale))
+        if not e <= TOL:
+            return f"dedup with scaled sink off by {e:.3g}"
+    return None
+
+
+def check_scaled_sink_reading(ref):
+    """sink_scaled=True: the sink logit is scale * sink (brute force with that
+    column, and the single-entry closed form logistic(s_j - scale*sink))."""
+    w = make_random(36, 2, 2, 4, 16, 20, 8, p_unused=0.2, scale=0.37)
+    kv = _kv(w)
+    sc = float(np.float32(w.scale))
+    z = sc * np.asarray(w.sink, np.float64)
+    got = ref(w.q, kv, w.sink, w.idxs, w.scale, sink_scaled=True)
+    e = _err(got, dense_masked(w.q, kv, z, w.idxs, w.scale))
+    if not e <= TOL:
+        return f"scaled sink brute force off by {e:.3g}"
+    if not _err(got, ref(w.q, kv, w.sink, w.idxs, w.scale)) > 1e-6:
+        return "scaling the sink made no difference"
+    q = bf16_bits_to_f32(w.q).astype(np.float64)
+    kvf = bf16_bits_to_f32(kv).astype(np.float64)
+    idx = np.full((w.B, w.T, 3), -1, np.int32)
+    idx[:, :, 1] = 4
+    out = ref(w.q, kv, w.sink, idx, w.scale, sink_scaled=True)
+    for b in range(w.B):
+        for t in range(w.T):
+            for h in range(w.H):
+                s = sc * float(q[b, t, h] @ kvf[b, 4])
+                g = 1.0 / (1.0 + math.exp(-(s - z[h])))
+                if not _err(out[b, t, h], g * kvf[b, 4]) <= TOL:
+                    return "single-entry closed form with a scaled sink"
+    return None
+
+
 BATTERY = [check_hand_worked, check_bruteforce, check_sdpa, check_weights_sum,
            check_permutation_and_padding, check_independence, check_bound,
-           check_closed_forms]
+           check_closed_forms, check_repeated_index_readings, check_scaled_sink_reading]
 
 
 def run_battery(ref):

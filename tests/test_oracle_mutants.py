@@ -23,6 +23,12 @@ MUTANTS = {
     "dot_product_short_by_one": ("for (int64_t d = 0; d < D; ++d)\n                    dot +=",
                                  "for (int64_t d = 0; d + 1 < D; ++d)\n                    dot +="),
     "sink_weight_doubled": ("double L = wz;", "double L = 2.0 * wz;"),
+    "dedup_flag_ignored": ("if (use[k] && (flags & ORACLE_DEDUP))", "if (use[k] && 0)"),
+    "dedup_always_applied": ("if (use[k] && (flags & ORACLE_DEDUP))", "if (use[k])"),
+    "sink_scale_flag_ignored": ("const double z = (flags & ORACLE_SINK_SCALED) ? sc * zraw : zraw;",
+                                "const double z = zraw;"),
+    "sink_scale_flag_always": ("const double z = (flags & ORACLE_SINK_SCALED) ? sc * zraw : zraw;",
+                               "const double z = sc * zraw;"),
 }
 
 
