@@ -49,6 +49,19 @@ constexpr int dma_step(int q, int ng, int nsteps) {
     return q * nsteps / ng + DMA_LAG < nsteps ? q * nsteps / ng + DMA_LAG : nsteps - 1;
 }
 constexpr int LIST_CAP = 2048;        // longest index list a workgroup compacts
+constexpr int LDS_BYTES = 160 * 1024; // LDS per compute unit (gfx950)
+
+// Static LDS of attn_fwd_kernel<D, NHQ, HT> (its ring, partial scores,
+// published weights and factors, per-wave counts); the compacted list comes on
+// top as dynamic LDS, 4 bytes per entry.
+constexpr size_t fwd_ring_slots(int NHQ) {
+    return 2 + (63 / (32 / (2 * NHQ)) >= 2 ? 2 : 63 / (32 / (2 * NHQ)));
+}
+constexpr size_t fwd_static_lds(int D, int NHQ, int HT) {
+    return fwd_ring_slots(NHQ) * 32 * (2 * D + 32) + (size_t)(2 * NHQ) * (2 * HT) * 64 * 16 +
+           (size_t)NHQ * HT * 1024 + (size_t)NHQ * HT * 64 + (size_t)(2 * NHQ) * 4;
+}
+size_t list_lds_bytes(int K) { return ((size_t)(K > 0 ? K : 1) * 4 + 15) / 16 * 16; }
 constexpr int MAX_SPLITS = 64;
 constexpr float LOG2E = 1.4426950408889634f;
 // The running max is only raised when a chunk beats it by more than this many
@@ -71,10 +84,10 @@ struct FwdParams {
     const int32_t *idxs;
     uint16_t *out;     // non-split path
     uint16_t *ws_o;    // split path: [Q, S, H, D] fp16, each split normalised by its ws_l
-                       // and divided by the power of two ws_x of its half row
+                       // and divided by the power of two ws_x of its row
     float *ws_m;       // [Q, S, H] running max, log2 units
     float *ws_l;       // [Q, S, H] denominator relative to ws_m
-    float *ws_x;       // [Q, S, H, 2] power-of-two scale of each half row of ws_o
+    float *ws_x;       // [Q, S, H] power-of-two scale of each row of ws_o
     int64_t N;
     int32_t T, H, K;
     int32_t S, HG, units, per_xcd, bs;  // see unit_of
@@ -297,50 +310,58 @@ __device__ __forceinline__ void wait_vm_ahead(int ahead) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// a7 / a8: epilogue shared by the attention kernels.  Lane (li, g) of wave
-// (hq, dh) holds O^T[dh*D/2 + 16u + 4g + i, h] of head tile t, with the
-// softmax state (m, lsum) of head h = hg*HWG + hq*HW + 16t + li.  Every output
-// (final, or a split's partial) is normalised by its own denominator, then
-// staged through LDS (HWG rows of 2D bytes at `stage_out`, which the caller
-// has freed with a barrier) so that each wave instruction stores whole rows:
-// the final output as bf16, a split's partial as fp16 scaled by a power of
-// two.  In LDS, 16-byte chunk c of head row hl sits at position c ^ swz(hl),
-// which keeps the 16 rows written by one store instruction on distinct banks.
-template <int D, int NHQ, int HT>
-__device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t (&o)[HT][D / 32],
-                                              const float (&m)[HT], const float (&lsum)[HT],
-                                              int qi, int s, int hg, LDS_AS uint8_t *stage_out) {
-    constexpr int NT = NHQ * 128;
-    constexpr int HW = 16 * HT;
-    constexpr int HWG = NHQ * HW;
-    constexpr int DTH = D / 32;
+// a7 / a8: epilogue shared by the attention kernels.  The workgroup holds
+// HWG = 16*NTL heads; wave w of NW holds the output columns
+// w*DW .. w*DW + DW - 1 (DW = D/NW) of every head: lane (li, g) holds
+// O^T[w*DW + 16u + 4g + i, 16t + li] in o[t][u][i].  mh / lh give each head's
+// running max (log2 units) and total denominator; red is scratch for NW*HWG
+// floats.  Every output (final, or a split's partial) is normalised by its own
+// denominator, then staged through LDS (HWG rows of 2D bytes at `stage_out`,
+// which the caller has freed with a barrier) so that each wave instruction
+// stores whole rows: the final output as bf16, a split's partial as fp16
+// divided by a power of two per row.  In LDS, 16-byte chunk c of head row hl
+// sits at position c ^ swz(hl), which keeps the 16 rows written by one store
+// instruction on distinct banks.
+template <int D, int NW, int NTL>
+__device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t (&o)[NTL][D / NW / 16],
+                                              const LDS_AS float *mh, const LDS_AS float *lh,
+                                              LDS_AS float *red, int qi, int s, int hg,
+                                              LDS_AS uint8_t *stage_out) {
+    constexpr int NT = NW * 64;
+    constexpr int HWG = 16 * NTL;
+    constexpr int DW = D / NW;
+    constexpr int NU = DW / 16;
     constexpr int C16 = D / 8;  // 16-byte chunks per 16-bit row
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int hq = wid >> 1, dh = wid & 1, g = lane >> 4, li = lane & 15;
+    const int g = lane >> 4, li = lane & 15;
     const int hbase = hg * HWG;
+    float inv[NTL];
 #pragma unroll
-    for (int t = 0; t < HT; ++t) {
-        const int h = hbase + hq * HW + 16 * t + li;
-        const bool h_ok = h < p.H;
-        const int hl = hq * HW + 16 * t + li;  // head row within the workgroup
-        float ltot = lsum[t] + shfl_xor_f(lsum[t], 16);
-        ltot += shfl_xor_f(ltot, 32);
-        float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
-        if (p.S == 1) {
-            if (p.sink != nullptr && h_ok) {
-                // the sink joins the softmax: M = max(m, sink), L = l 2^(m-M) + 2^(sink-M)
-                const float zs = p.sink[h] * LOG2E;
-                const float M = fmaxf(m[t], zs);
-                const float alpha = m[t] == -INFINITY ? 0.f : exp2_fast(m[t] - M);
-                inv = alpha / (ltot * alpha + exp2_fast(zs - M));
-            }
+    for (int t = 0; t < NTL; ++t) {
+        const int hl = 16 * t + li;
+        const int h = hbase + hl;
+        const float ltot = lh[hl], mm = mh[hl];
+        inv[t] = ltot > 0.f ? 1.f / ltot : 0.f;
+        if (p.S == 1 && p.sink != nullptr && h < p.H) {
+            // the sink joins the softmax: M = max(m, sink), L = l 2^(m-M) + 2^(sink-M);
+            // nothing to attend to (m and the sink both -inf) gives 0
+            const float zs = p.sink[h] * LOG2E;
+            const float M = fmaxf(mm, zs);
+            const float alpha = mm == -INFINITY ? 0.f : exp2_fast(mm - M);
+            inv[t] = M == -INFINITY ? 0.f : alpha / (ltot * alpha + exp2_fast(zs - M));
+        }
+    }
+    if (p.S == 1) {
 #pragma unroll
-            for (int u = 0; u < DTH; ++u) {
-                const int col = dh * (D / 2) + 16 * u + 4 * g;  // first of 4 columns
+        for (int t = 0; t < NTL; ++t) {
+            const int hl = 16 * t + li;
+            LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int col = wid * DW + 16 * u + 4 * g;  // first of 4 columns
                 const int pos = (col >> 3) ^ swz<C16>(hl);
-                float v0 = o[t][u][0] * inv, v1 = o[t][u][1] * inv;
-                float v2 = o[t][u][2] * inv, v3 = o[t][u][3] * inv;
+                float v0 = o[t][u][0] * inv[t], v1 = o[t][u][1] * inv[t];
+                float v2 = o[t][u][2] * inv[t], v3 = o[t][u][3] * inv[t];
                 if (col >= D - p.rd) {  // rotary dims: pairs (col, col+1), (col+2, col+3)
                     const int64_t pr = (int64_t)(qi % p.T) * (p.rd / 2) + (col - (D - p.rd)) / 2;
                     rotate_back2(v0, v1, v2, v3, *(const float4 *)(p.rope + 2 * pr));
@@ -348,39 +369,51 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
                 const u32x2_t w = {pack2_bf16(v0, v1), pack2_bf16(v2, v3)};
                 *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
             }
-        } else {
-            // A split's partial: fp16 rows (11 significant bits) scaled by a
-            // power of two per (head, half row) so that |value| < 2^15 never
-            // overflows.
-            // inv >= 0 and rounding is monotonic, so max |o| * inv is exactly
-            // max |o * inv|
+        }
+    } else {
+        // A split's partial: fp16 rows (11 significant bits) divided by a power
+        // of two 2^e per (head, split), chosen from the row's largest magnitude
+        // so that it lands in [2^14, 2^15): no overflow for large rows, no
+        // subnormals for small ones.  inv >= 0 and rounding is monotonic, so
+        // max |o| * inv is exactly max |o * inv|.
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
             float amax = 0.f;
 #pragma unroll
-            for (int u = 0; u < DTH; ++u)
+            for (int u = 0; u < NU; ++u)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[t][u][i]));
             amax = fmaxf(amax, shfl_xor_f(amax, 16));
             amax = fmaxf(amax, shfl_xor_f(amax, 32));
-            amax *= inv;
-            int ex = 0;
-            if (amax < INFINITY) (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1)
-            const int e = ex > 15 ? ex - 15 : 0;
-            const float down = ldexpf(inv, -e);
+            if (g == 0) red[wid * HWG + 16 * t + li] = amax;
+        }
+        __syncthreads();
 #pragma unroll
-            for (int u = 0; u < DTH; ++u) {
-                const int col = dh * (D / 2) + 16 * u + 4 * g;
+        for (int t = 0; t < NTL; ++t) {
+            const int hl = 16 * t + li;
+            const int h = hbase + hl;
+            float amax = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) amax = fmaxf(amax, red[w * HWG + hl]);
+            amax *= inv[t];
+            int ex = 15;  // amax = f 2^ex, f in [0.5, 1); zero or non-finite rows: e = 0
+            if (amax > 0.f && amax < INFINITY) (void)frexpf(amax, &ex);
+            const int e = ex - 15 > -100 ? ex - 15 : -100;
+            const float down = ldexpf(inv[t], -e);
+            LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int col = wid * DW + 16 * u + 4 * g;
                 const int pos = (col >> 3) ^ swz<C16>(hl);
                 const u32x2_t w = {pack2_f16(o[t][u][0] * down, o[t][u][1] * down),
                                    pack2_f16(o[t][u][2] * down, o[t][u][3] * down)};
                 *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
             }
-            if (g == 0 && h_ok) {
+            if (wid == 0 && g == 0 && h < p.H) {
                 const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
-                p.ws_x[slot * 2 + dh] = ldexpf(1.f, e);
-                if (dh == 0) {
-                    p.ws_m[slot] = m[t];
-                    p.ws_l[slot] = ltot;
-                }
+                p.ws_x[slot] = ldexpf(1.f, e);
+                p.ws_m[slot] = mh[hl];
+                p.ws_l[slot] = lh[hl];
             }
         }
     }
@@ -487,16 +520,21 @@ __device__ void expand_fp4(LDS_AS uint8_t *T, int RS, int rec, const int32_t *li
 // served by a pair of waves, one per half of the head dimension.  For QK^T a
 // wave sums over its half of d and the pair adds the two partial scores
 // through LDS, so both waves of the pair hold the same scores and run the same
-// softmax; for PV each wave produces its half of the output columns.  A wave
-// holds HT tiles of 16 heads: every K or V operand it reads from LDS feeds HT
-// MFMAs, so LDS read traffic per chunk falls as 1/HT, at the cost of HT x
-// (16 x D/2) accumulators and query values in registers.
+// softmax; one of them publishes the bf16 weights (and the rescale factor of
+// the running max) in LDS.  For PV every wave takes D/NW output columns of all
+// the workgroup's heads, so each V operand read from LDS (a transpose read,
+// the slowest LDS access) feeds one MFMA per head tile of the workgroup and
+// every row of V is read from LDS once per chunk.  The PV of chunk c runs
+// after the barrier that opens chunk c + 1, so publishing the weights needs no
+// barrier of its own.  A pair holds HT tiles of 16 heads for QK^T: every K
+// operand it reads feeds HT MFMAs.
 template <int D, int NHQ, int HT, bool FP4>
 __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     constexpr int NW = 2 * NHQ;            // waves per workgroup
     constexpr int NT = NW * 64;
-    constexpr int HW = 16 * HT;            // heads per wave
+    constexpr int HW = 16 * HT;            // heads per wave pair (QK^T, softmax)
     constexpr int HWG = NHQ * HW;          // heads per workgroup
+    constexpr int NTL = HWG / 16;          // head tiles per workgroup (PV)
     constexpr int ROWB = D * 2;            // bytes per row
     constexpr int CPR = D / 8;             // 16-byte chunks per row
     // Ring rows are padded to RS bytes: with RS = 2D + 32 the 16-byte slot of
@@ -508,18 +546,27 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     constexpr int RS = ROWB + 32;          // LDS bytes per ring row
     constexpr int IPW = KC / NW;           // DMA wave instructions (one row each) per wave
     constexpr int DSH = D / 64;            // MFMA k-steps over one half of d
-    constexpr int DTH = D / 32;            // 16-wide output tiles in one half of d
+    constexpr int DW = D / NW;             // output columns per wave (PV)
+    constexpr int NU = DW / 16;            // 16-wide output tiles per wave
     // LDS ring depth (chunks): up to 4, as long as the DMA instructions of the
     // chunks in flight fit the 6-bit vmcnt
     constexpr int NBUF = 2 + (63 / IPW >= 2 ? 2 : 63 / IPW);
     static_assert(CPR >= 16 && 64 % CPR == 0, "row swizzle needs D in {128, 256, 512}");
     static_assert(KC % NW == 0, "DMA instructions must split evenly over the waves");
     static_assert(HT == 1 || HT == 2, "one or two head tiles per wave");
+    static_assert(NU >= 1 && DW % 16 == 0, "whole 16-column tiles per wave");
 
     __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][KC * RS];
     __shared__ __attribute__((aligned(16))) f32x4_t xbuf[NW][2 * HT][64];  // partial scores
-    __shared__ int32_t list[LIST_CAP];
+    __shared__ __attribute__((aligned(16))) u32x4_t pbuf[NTL][64];         // bf16 weights per head tile
+    __shared__ float abuf[NTL][16];                                        // rescale factors
     __shared__ int32_t cnt[NW];
+    extern __shared__ int32_t list[];  // the compacted list (K entries, dynamic)
+    static_assert(sizeof(xbuf) >= (2 + NW) * HWG * sizeof(float), "epilogue state fits in xbuf");
+    static_assert(NBUF == fwd_ring_slots(NHQ) &&
+                  sizeof(tile) + sizeof(xbuf) + sizeof(pbuf) + sizeof(abuf) + sizeof(cnt) ==
+                      fwd_static_lds(D, NHQ, HT),
+                  "the host's LDS figure matches the declarations");
 
     const int bid = blockIdx.x;
     const int unit = unit_of(bid, p.units, p.bs);
@@ -677,14 +724,59 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     // Softmax state of head hw0 + 16t + li (log2 units), identical in both
     // waves of the pair.  The sink is folded in by the epilogue.
     float m[HT], lsum[HT];
-    f32x4_t o[HT][DTH];
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
         m[t] = -INFINITY;
         lsum[t] = 0.f;
-#pragma unroll
-        for (int u = 0; u < DTH; ++u) o[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // O^T over this wave's output columns for every head tile of the workgroup
+    f32x4_t o[NTL][NU];
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int u = 0; u < NU; ++u) o[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // a6: O^T[d, h] += V^T[d, j] P^T[j, h] for this wave's columns, chunk cc,
+    // with the weights and rescale factors the pairs published.  A operand
+    // through transpose loads: lane i of block g addresses row 4g + i/4 (and
+    // +16), columns 16u + 4(i%4) .. +3; the load hands lane i column 16u + i of
+    // rows 4g..4g+3, matching the weight slots j = 4g + e and 16 + 4g + e.
+    // Each V operand feeds NTL MFMAs (pipelined by hand: transpose pair u + PVP
+    // is requested right after the MFMAs of pair u).
+    auto pv_chunk = [&](int cc) {
+        const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[cc % NBUF][0];
+        bf16x8_t pb[NTL];
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            pb[t] = __builtin_bit_cast(bf16x8_t, pbuf[t][lane]);
+            const float a = abuf[t][li];
+            if (__ballot(a != 1.f)) {
+#pragma unroll
+                for (int u = 0; u < NU; ++u) o[t][u] *= a;
+            }
+        }
+        constexpr int PVP = NU < 4 ? NU : 4;
+        const int r0 = 4 * g + (li >> 2);
+        const LDS_AS uint8_t *R0 = T + r0 * RS + (li & 3) * 8;
+        const LDS_AS uint8_t *R1 = R0 + 16 * RS;
+        auto vload = [&](int u) {
+            const int pos = (wid * NU + u) * 32;
+            const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R0 + pos));
+            const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R1 + pos));
+            return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8_t va[PVP];
+#pragma unroll
+        for (int u = 0; u < PVP; ++u) va[u] = vload(u);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int t = 0; t < NTL; ++t)
+                o[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u % PVP], pb[t], o[t][u], 0, 0, 0);
+            if (u + PVP < NU) va[u % PVP] = vload(u + PVP);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
 
     LDS_AS f32x4_t *xmine = (LDS_AS f32x4_t *)&xbuf[wid][0][lane];
     const LDS_AS f32x4_t *xpeer = (const LDS_AS f32x4_t *)&xbuf[wid ^ 1][0][lane];
@@ -711,8 +803,10 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         // chunk c has landed once at most the chunk after it is pending
         wait_vm_ahead<IPW, 1>(min(1, nchunks - 1 - c));
         __syncthreads();
-        // chunk c + 2 goes into slot (c + 2) % NBUF, last read by chunk c - 2,
-        // which every wave finished before the barrier above
+        // PV of chunk c - 1 (its weights were published before this barrier)
+        if (c > 0) pv_chunk(c - 1);
+        // chunk c + 2 goes into slot (c + 2) % NBUF, last read by the PV of
+        // chunk c - 2, which every wave finished before the barrier above
         const int rq = c == 0 ? 1 : c + 2;  // first chunk requested in this QK^T
         const bool do_stage = rq < nchunks;
         const bool two = c == 0 && 2 < nchunks;  // chunk 2 as well
@@ -785,7 +879,8 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         // of head tile t.  The kept max m only moves when a score beats it by
         // more than MAX_SLACK; a per-lane check and one ballot decide that, and
         // the exact chunk max (two cross-lane reductions) is only taken then.
-        bf16x8_t pb[HT];
+        // Wave dh == 0 of the pair publishes the bf16 weights and the factor
+        // that rescales the accumulators (1 when the max stayed).
 #pragma unroll
         for (int t = 0; t < HT; ++t) {
             float sv[8];
@@ -801,15 +896,14 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             }
             float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                                fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            float alpha = 1.f;
             if (__ballot(lmax > m[t] + MAX_SLACK)) {
                 float cmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
                 cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
                 const bool raise = cmax > m[t] + MAX_SLACK;
                 const float mnew = raise ? cmax : m[t];
-                const float alpha = exp2_fast(m[t] - mnew);
+                alpha = exp2_fast(m[t] - mnew);
                 lsum[t] *= alpha;
-#pragma unroll
-                for (int u = 0; u < DTH; ++u) o[t][u] *= alpha;
                 m[t] = mnew;
             }
             // The weights enter the value product as bf16; the denominator sums
@@ -824,55 +918,43 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             for (int e = 0; e < 4; ++e)
                 psum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
             lsum[t] += psum;
-            pb[t] = __builtin_bit_cast(bf16x8_t, pw);
-        }
-
-        // a6: O^T[d, h] += V^T[d, j] P^T[j, h] for this wave's half of d.
-        // A operand through transpose loads: lane i of block g addresses row
-        // 4g + i/4 (and +16), columns 16t + 4(i%4) .. +3; the load hands lane i
-        // column 16t + i of rows 4g..4g+3, matching the weight slots
-        // j = 4g + e and 16 + 4g + e.  Each V operand feeds HT MFMAs.
-        // (pipelined by hand like QK^T: transpose pair u + PVP is requested
-        // right after the MFMAs of pair u)
-        {
-            constexpr int PVP = 4;
-            const int r0 = 4 * g + (li >> 2);
-            const LDS_AS uint8_t *R0 = T + r0 * RS + (li & 3) * 8;
-            const LDS_AS uint8_t *R1 = R0 + 16 * RS;
-            auto vload = [&](int u) {
-                const int pos = (dh * DTH + u) * 32;
-                const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R0 + pos));
-                const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R1 + pos));
-                return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            };
-            bf16x8_t va[PVP];
-#pragma unroll
-            for (int u = 0; u < PVP; ++u) va[u] = vload(u);
-#pragma unroll
-            for (int u = 0; u < DTH; ++u) {
-#pragma unroll
-                for (int t = 0; t < HT; ++t)
-                    o[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u % PVP], pb[t], o[t][u], 0, 0, 0);
-                if (u + PVP < DTH) va[u % PVP] = vload(u + PVP);
-                __builtin_amdgcn_sched_barrier(0);
+            if (dh == 0) {
+                pbuf[hq * HT + t][lane] = pw;
+                if (g == 0) abuf[hq * HT + t][li] = alpha;
             }
         }
     }
 
-    // a7 / a8: epilogue
+    // a7 / a8: epilogue.  The last chunk's PV, then each pair publishes the
+    // running max and total denominator of its heads for every wave.
     static_assert(HWG * D * 2 <= NBUF * KC * RS, "output staging fits in the ring");
+    __syncthreads();
+    if (nchunks > 0) pv_chunk(nchunks - 1);
+    LDS_AS float *mh = (LDS_AS float *)&xbuf[0][0][0];
+    LDS_AS float *lh = mh + HWG;
+    LDS_AS float *red = lh + HWG;
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+        float ltot = lsum[t] + shfl_xor_f(lsum[t], 16);
+        ltot += shfl_xor_f(ltot, 32);
+        if (dh == 0 && g == 0) {
+            mh[hq * HW + 16 * t + li] = m[t];
+            lh[hq * HW + 16 * t + li] = ltot;
+        }
+    }
     __syncthreads();  // every wave is done with the ring; reuse it for staging
-    store_outputs<D, NHQ, HT>(p, o, m, lsum, qi, s, hg, (LDS_AS uint8_t *)&tile[0][0]);
+    store_outputs<D, NW, NTL>(p, o, mh, lh, red, qi, s, hg, (LDS_AS uint8_t *)&tile[0][0]);
 }
 
 // Many-query variant, for launches with at least two workgroups per compute
 // unit (prefill), where MFMA throughput rather than gather depth decides.
 // Same steps and results as attn_fwd_kernel; the work is split differently:
-//   * a pair of waves serves 32 heads.  For QK^T and the softmax each wave
-//     takes one tile of 16 heads over the whole of d (no partial scores to
-//     add up); the pair then swaps its bf16 weights (and rescale factors)
-//     through LDS, and for PV each wave takes one half of d for both tiles,
-//     so every V operand read from LDS feeds two MFMAs;
+//   * for QK^T and the softmax each wave takes one tile of 16 heads over the
+//     whole of d (no partial scores to add up); the waves then publish their
+//     bf16 weights (and rescale factors) in LDS, and for PV each wave takes
+//     D/NW output columns of every head of the workgroup, so every V operand
+//     read from LDS (a transpose read, the slowest LDS access) feeds one MFMA
+//     per head tile and each row of V is read from LDS once per chunk;
 //   * a 2-chunk ring of 32 padded rows, the weight exchange and the list
 //     (compacted in place, sized by K in dynamic LDS) take about 75 KB of
 //     LDS, so two workgroups share a compute unit and one's softmax,
@@ -889,13 +971,16 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     constexpr int NB = 2;                  // ring chunks
     constexpr int IPW = KC / NW;           // DMA instructions (one row each) per wave per chunk
     constexpr int DS = D / 32;             // MFMA k-steps over d
-    constexpr int DTH = D / 32;            // 16-wide output tiles in one half of d
+    constexpr int NTL = NW;                // head tiles per workgroup (wave w owns tile w)
+    constexpr int HWG = 16 * NTL;
+    constexpr int DW = D / NW;             // output columns per wave (PV)
+    constexpr int NU = DW / 16;            // 16-wide output tiles per wave
     static_assert(KC % NW == 0 && IPW <= 63, "ring shape");
     static_assert(NHQ * HP * D * 2 <= NB * KC * RS, "output staging fits in the ring");
 
     __shared__ __attribute__((aligned(16))) uint8_t tile[NB][KC * RS];
-    __shared__ __attribute__((aligned(16))) u32x4_t xp[NW][64];  // bf16 weights of the tile
-    __shared__ float xa[NW][64];                                  // rescale factor / final state
+    __shared__ __attribute__((aligned(16))) u32x4_t xp[NW][64];  // bf16 weights of the tiles
+    __shared__ float xa[NW][16];                                  // rescale factors
     __shared__ int32_t cnt[NW];
     extern __shared__ int32_t list[];  // K entries: raw, then compacted in place
 
@@ -994,11 +1079,11 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     }
 
     float m = -INFINITY, lsum = 0.f;  // softmax state of head hown (log2 units)
-    f32x4_t o[HT][DTH];               // O^T of both tiles over this wave's half of d
+    f32x4_t o[NTL][NU];               // O^T of every head tile over this wave's columns
 #pragma unroll
-    for (int t = 0; t < HT; ++t)
+    for (int t = 0; t < NTL; ++t)
 #pragma unroll
-        for (int u = 0; u < DTH; ++u) o[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < NU; ++u) o[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int c = 0; c < nchunks; ++c) {
         // chunk c has landed once at most the chunk after it is pending
@@ -1076,35 +1161,32 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
             psum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
         lsum += psum;
 
-        // the pair swaps weights and rescale factors
+        // every wave publishes its tile's weights and rescale factor
         xp[wid][lane] = pw;
         if (g == 0) xa[wid][li] = alpha;
         __syncthreads();
-        const u32x4_t pp = xp[wid ^ 1][lane];
-        const float alpha_p = xa[wid ^ 1][li];
-        const bf16x8_t p0 = __builtin_bit_cast(bf16x8_t, w == 0 ? pw : pp);
-        const bf16x8_t p1 = __builtin_bit_cast(bf16x8_t, w == 0 ? pp : pw);
-        const float a0 = w == 0 ? alpha : alpha_p, a1 = w == 0 ? alpha_p : alpha;
-        if (__ballot(a0 != 1.f)) {
+        bf16x8_t pb[NTL];
 #pragma unroll
-            for (int u = 0; u < DTH; ++u) o[0][u] *= a0;
-        }
-        if (__ballot(a1 != 1.f)) {
+        for (int t = 0; t < NTL; ++t) {
+            pb[t] = __builtin_bit_cast(bf16x8_t, t == wid ? pw : xp[t][lane]);
+            const float a = xa[t][li];
+            if (__ballot(a != 1.f)) {
 #pragma unroll
-            for (int u = 0; u < DTH; ++u) o[1][u] *= a1;
+                for (int u = 0; u < NU; ++u) o[t][u] *= a;
+            }
         }
 
-        // a6: O^T[d, h] += V^T[d, j] P^T[j, h] over this wave's half of d; the
-        // transpose loads hand lane (li, g) column 16tt + li of rows 4g..4g+3
+        // a6: O^T[d, h] += V^T[d, j] P^T[j, h] over this wave's columns; the
+        // transpose loads hand lane (li, g) column 16u + li of rows 4g..4g+3
         // and 16+4g..16+4g+3, the k-slots of its weights
         // (pipelined by hand like QK^T: transpose pair u + PVP is loaded right
-        // after the two MFMAs of pair u)
+        // after the MFMAs of pair u)
         {
-            constexpr int PVP = 3;
+            constexpr int PVP = NU < 3 ? NU : 3;
             const LDS_AS uint8_t *R0 = T + (4 * g + (li >> 2)) * RS + (li & 3) * 8;
             const LDS_AS uint8_t *R1 = R0 + 16 * RS;
             auto vload = [&](int u) {
-                const int off = (w * DTH + u) * 32;
+                const int off = (wid * NU + u) * 32;
                 const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R0 + off));
                 const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t *)(R1 + off));
                 return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -1113,31 +1195,36 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 #pragma unroll
             for (int u = 0; u < PVP; ++u) va[u] = vload(u);
 #pragma unroll
-            for (int u = 0; u < DTH; ++u) {
-                o[0][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u % PVP], p0, o[0][u], 0, 0, 0);
-                o[1][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u % PVP], p1, o[1][u], 0, 0, 0);
-                if (u + PVP < DTH) va[u % PVP] = vload(u + PVP);
+            for (int u = 0; u < NU; ++u) {
+#pragma unroll
+                for (int t = 0; t < NTL; ++t)
+                    o[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u % PVP], pb[t], o[t][u], 0, 0, 0);
+                if (u + PVP < NU) va[u % PVP] = vload(u + PVP);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
 
-    // a7 / a8: epilogue.  The pair swaps its final softmax state so that each
-    // wave can normalise both tiles of its half of d.
+    // a7 / a8: epilogue.  Every wave publishes the running max and total
+    // denominator of its tile's heads for the others.
     __syncthreads();  // every wave is done with the ring and the exchange buffers
-    xa[wid][lane] = lsum;
-    if (g == 0) *(LDS_AS float *)&xp[wid][li] = m;
+    LDS_AS float *mh = (LDS_AS float *)&xp[0][0];
+    LDS_AS float *lh = mh + HWG;
+    LDS_AS float *red = lh + HWG;
+    static_assert(sizeof(xp) >= (2 + NW) * HWG * sizeof(float), "epilogue state fits in xp");
+    float ltot = lsum + shfl_xor_f(lsum, 16);
+    ltot += shfl_xor_f(ltot, 32);
+    if (g == 0) {
+        mh[16 * wid + li] = m;
+        lh[16 * wid + li] = ltot;
+    }
     __syncthreads();
-    const float lsum_p = xa[wid ^ 1][lane];
-    const float m_p = *(const LDS_AS float *)&xp[wid ^ 1][li];
-    const float mt[HT] = {w == 0 ? m : m_p, w == 0 ? m_p : m};
-    const float lt[HT] = {w == 0 ? lsum : lsum_p, w == 0 ? lsum_p : lsum};
-    store_outputs<D, NHQ, HT>(p, o, mt, lt, qi, s, hg, (LDS_AS uint8_t *)&tile[0][0]);
+    store_outputs<D, NW, NTL>(p, o, mh, lh, red, qi, s, hg, (LDS_AS uint8_t *)&tile[0][0]);
 }
 
 // a9: log-sum-exp merge of the splits.  Split s holds p_s (its output
 // normalised by its own denominator l_s; fp16 times the power of two x_s of
-// the half row), its max m_s and l_s (log2 units).  With
+// the row), its max m_s and l_s (log2 units).  With
 // M = max(sink, max_s m_s) and L = 2^(sink - M) + sum_s 2^(m_s - M) l_s,
 // out = sum_s (2^(m_s - M) l_s / L) p_s.
 //
@@ -1163,7 +1250,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     constexpr int RWG = 4 * RPW;     // rows per workgroup
     constexpr int SB = 8;            // splits per batch of row loads
     constexpr int SPL = MAX_SPLITS / LPR > 0 ? MAX_SPLITS / LPR : 1;  // scalar slots per lane
-    __shared__ f32x2_t coef[RWG][MAX_SPLITS];
+    __shared__ float coef[RWG][MAX_SPLITS];
 
     const int bid = blockIdx.x;
     // reversed blocks per XCD, like the attention kernels' unit order (the
@@ -1177,7 +1264,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     const int64_t qi = ok ? qh / H : 0;
     const int h = ok ? (int)(qh % H) : 0;
     const int c8 = sl * 8;
-    const int half = c8 >= D / 2 ? 1 : 0;
     const int64_t slot0 = qi * S * H + h;    // slot of split j: slot0 + j * H
 
     // The partials are read once: non-temporal loads with up to four splits
@@ -1198,7 +1284,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         cs1 = *(const float4 *)(f + 4);
     }
     // lane sl holds the scalars of splits sl, sl + LPR, ...
-    float mj[SPL], lj[SPL], x0[SPL], x1[SPL];
+    float mj[SPL], lj[SPL], xj[SPL];
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
         const int j = sl + k * LPR;
@@ -1206,8 +1292,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         const int64_t slot = slot0 + (int64_t)j * H;
         mj[k] = has ? ws_m[slot] : -INFINITY;
         lj[k] = has ? ws_l[slot] : 0.f;
-        x0[k] = has ? ws_x[slot * 2] : 0.f;
-        x1[k] = has ? ws_x[slot * 2 + 1] : 0.f;
+        xj[k] = has ? ws_x[slot] : 0.f;
     }
     const float mz = ok && sink != nullptr ? sink[h] * LOG2E : -INFINITY;
     float mx = mz;
@@ -1229,7 +1314,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         const int j = sl + k * LPR;
         if (j < S) {
             const float c = mx != -INFINITY ? exp2_fast(mj[k] - mx) * lj[k] * invL : 0.f;
-            coef[rw][j] = f32x2_t{c * x0[k], c * x1[k]};
+            coef[rw][j] = c * xj[k];
         }
     }
     __syncthreads();
@@ -1244,8 +1329,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
             if (j0 + j < S) {
-                const f32x2_t cc = coef[rw][j0 + j];
-                const float c = half ? cc[1] : cc[0];
+                const float c = coef[rw][j0 + j];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const f32x2_t f = unpack2_f16(v[j][e]);
@@ -1614,6 +1698,8 @@ int64_t queries(const sa_dims *d) { return (int64_t)d->B * d->T; }
 WgShape shape_for(const sa_dims *d, int S) {
     const WgShape base = shape_for(d->H);
     if (base.nhq != 4) return base;
+    // the 64-head workgroup's LDS leaves room for lists of up to ~1970 entries
+    if (fwd_static_lds(d->D, 4, 1) + list_lds_bytes(d->K) > (size_t)LDS_BYTES) return WgShape{2, 1};
     const int cus = device_cu_count();
     const int64_t narrow_units = queries(d) * ((d->H + 31) / 32) * S;
     return cus > 0 && narrow_units <= cus ? WgShape{2, 1} : base;
@@ -1636,7 +1722,7 @@ WsLayout ws_layout(const sa_dims *d, int S) {
     w.m_off = up(slots * d->D * sizeof(uint16_t));
     w.l_off = w.m_off + up(slots * sizeof(float));
     w.x_off = w.l_off + up(slots * sizeof(float));
-    w.bytes = w.x_off + up(slots * 2 * sizeof(float));
+    w.bytes = w.x_off + up(slots * sizeof(float));
     return w;
 }
 
@@ -1675,10 +1761,11 @@ hipError_t launch_fwd(const FwdParams &p, hipStream_t stream) {
     const int grid = 8 * p.per_xcd;
     // bf16 rows only, or FP4 records in the second source (a separate build of
     // the kernel, so the bf16 one carries none of the expansion code)
+    const size_t lb = list_lds_bytes(p.K);
     if (p.rec2 > 0)
-        hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ, HT, true>), dim3(grid), dim3(NHQ * 128), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ, HT, true>), dim3(grid), dim3(NHQ * 128), lb, stream, p);
     else
-        hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ, HT, false>), dim3(grid), dim3(NHQ * 128), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<D, NHQ, HT, false>), dim3(grid), dim3(NHQ * 128), lb, stream, p);
     return hipGetLastError();
 }
 
