@@ -64,8 +64,12 @@ enum sa_status {
     SA_ERR_UNSUPPORTED = 3, /* D or K outside what the kernels are built for */
     SA_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
     SA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than sparse_attn_workspace_bytes */
-    SA_ERR_SPLITS = 6,      /* num_splits outside [0, 64] */
-    SA_ERR_HIP = 7          /* a HIP call failed (device query or kernel launch) */
+    SA_ERR_INDEX_RANGE = 6, /* checked mode: a list holds an entry >= N.  The enqueue-only entry
+                               points never return it (they cannot read device data);
+                               sparse_attn_check_idxs counts such entries on the device, and a
+                               caller that reads the count reports this code */
+    SA_ERR_HIP = 7,         /* a HIP call failed (device query or kernel launch) */
+    SA_ERR_SPLITS = 8       /* num_splits outside [0, 64] (the *_splits entry points) */
 };
 
 /* Number of index-range splits the library picks when num_splits is 0: one
@@ -74,24 +78,45 @@ enum sa_status {
  * negative sa_status on bad dims or a failed device query. */
 int32_t sparse_attn_plan_splits(const sa_dims *d);
 
-/* Bytes of workspace sparse_attn_fwd needs for `num_splits` (0 = the planned
- * count): 0 for one split, else each split's output normalised by its own
- * denominator as fp16 [B*T, S, H, D] (each half row divided by a power of two
- * so that no value overflows), its running max (log2 units) and denominator,
- * float32 [B*T, S, H] each, and the half-row scales, float32 [B*T, S, H, 2];
- * every part padded to 256 bytes.  Returns 0 on bad dims. */
-size_t sparse_attn_workspace_bytes(const sa_dims *d, int32_t num_splits);
+/* Bytes of workspace sparse_attn_fwd needs for the split count the library
+ * plans for these dims (sparse_attn_plan_splits): 0 when one split is planned.
+ * Returns 0 on bad dims. */
+size_t sparse_attn_workspace_bytes(const sa_dims *d);
 
-/* The whole step: out = sparse_attn(q, kv, sink, idxs, scale).
- * num_splits: 0 = planned (one split when workspace is NULL), else 1..64.
+/* Bytes of workspace for `num_splits` splits (0 = the planned count): 0 for one
+ * split, else each split's output normalised by its own denominator as fp16
+ * [B*T, S, H, D] (each row divided by a power of two chosen from its largest
+ * magnitude, so that no value overflows or sinks into fp16 subnormals), its
+ * running max (log2 units), its denominator and the row's scale, float32
+ * [B*T, S, H] each, and the per-query split plan, int32 [B*T]; every part
+ * padded to 256 bytes.  Returns 0 on bad dims or num_splits outside [0, 64]. */
+size_t sparse_attn_workspace_bytes_splits(const sa_dims *d, int32_t num_splits);
+
+/* The whole step: out = sparse_attn(q, kv, sink, idxs, scale), the call of the
+ * pages' Attention.forward excerpt with the dims and a workspace made explicit.
+ * workspace NULL: one split (always correct, no workspace).  Otherwise the
+ * planned split count (sparse_attn_plan_splits), which needs
+ * workspace_bytes >= sparse_attn_workspace_bytes(d), else SA_ERR_WORKSPACE.
  * With more than one split the index list of each query is cut into
  * contiguous ranges of its valid entries, each range is reduced by its own
- * workgroup into partial (output, max, denominator) in `workspace`, and a
- * second kernel merges the partials with the sink (log-sum-exp combine).
- * Every split count gives the same result up to float32 rounding. */
+ * workgroup into a partial (output, max, denominator) in `workspace`, and a
+ * second kernel merges the partials with the sink (log-sum-exp combine).  How
+ * many ranges a query uses follows its own count of valid entries (a query
+ * with n of K entries valid uses ceil(n S / K) of the S split slots), decided on
+ * the device.  The partials hold the output in fp16 (11 significant bits,
+ * scaled per row), so split counts agree to about 2^-11 of each row's largest
+ * value before the final bf16 rounding. */
 int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int32_t *idxs,
-                    float scale, void *out, const sa_dims *d, int32_t num_splits,
-                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+                    float scale, void *out, const sa_dims *d, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* sparse_attn_fwd with an explicit split count: num_splits 0 = planned (one
+ * split when workspace is NULL), else 1..64 (SA_ERR_SPLITS outside [0, 64]);
+ * with more than one split the workspace must hold
+ * sparse_attn_workspace_bytes_splits(d, num_splits) bytes. */
+int sparse_attn_fwd_splits(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                           float scale, void *out, const sa_dims *d, int32_t num_splits,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The step followed by the inverse rotary step on the output (DeepSeek-V4.1
  * pages, "Output projection" page, Attention.forward excerpt:
@@ -107,7 +132,7 @@ int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int3
  * before the one bf16 rounding (the unfused pair of calls rounds twice).  The
  * first D - rd dims equal sparse_attn_fwd's bit for bit.  SA_ERR_SHAPE for a
  * bad rd, SA_ERR_NULL for freqs NULL with rd > 0, SA_ERR_ALIGN for freqs not
- * 16-byte aligned; other arguments as sparse_attn_fwd. */
+ * 16-byte aligned; other arguments as sparse_attn_fwd_splits. */
 int sparse_attn_fwd_rope(const void *q, const void *kv, const float *sink, const int32_t *idxs,
                          float scale, const float *freqs, int32_t rd, void *out, const sa_dims *d,
                          int32_t num_splits, void *workspace, size_t workspace_bytes,
@@ -124,7 +149,7 @@ int sparse_attn_fwd_rope(const void *q, const void *kv, const float *sink, const
  * result equals sparse_attn_fwd on the concatenated rows, bit for bit.
  * kv_win may be NULL when W == 0 and kv_cmp when W == N; both 16-byte aligned.
  * SA_ERR_SHAPE when W is outside [0, N] or a buffer has too few rows.  Other
- * arguments, checks and behaviour as sparse_attn_fwd. */
+ * arguments, checks and behaviour as sparse_attn_fwd_splits. */
 int sparse_attn_fwd_2src(const void *q, const void *kv_win, int32_t win_rows, const void *kv_cmp,
                          int32_t cmp_rows, int32_t W, const float *sink, const int32_t *idxs,
                          float scale, void *out, const sa_dims *d, int32_t num_splits,
@@ -153,7 +178,7 @@ int sparse_attn_fwd_2src_fp4(const void *q, const void *kv_win, int32_t win_rows
 
 /* First half of the split path (num_splits >= 2): writes the partials of every
  * split into `workspace` and nothing into out.  Same arguments and checks as
- * sparse_attn_fwd, without out. */
+ * sparse_attn_fwd_splits, without out. */
 int sparse_attn_fwd_partial(const void *q, const void *kv, const int32_t *idxs, float scale,
                             const sa_dims *d, int32_t num_splits, void *workspace,
                             size_t workspace_bytes, hipStream_t stream);

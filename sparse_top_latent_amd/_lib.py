@@ -14,7 +14,9 @@ LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
 SYMBOLS = (
     "sparse_attn_plan_splits",
     "sparse_attn_workspace_bytes",
+    "sparse_attn_workspace_bytes_splits",
     "sparse_attn_fwd",
+    "sparse_attn_fwd_splits",
     "sparse_attn_fwd_rope",
     "sparse_attn_fwd_2src",
     "sparse_attn_fwd_2src_fp4",
@@ -28,7 +30,9 @@ SYMBOLS = (
 )
 
 STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_UNSUPPORTED",
-          4: "SA_ERR_ALIGN", 5: "SA_ERR_WORKSPACE", 6: "SA_ERR_SPLITS", 7: "SA_ERR_HIP"}
+          4: "SA_ERR_ALIGN", 5: "SA_ERR_WORKSPACE", 6: "SA_ERR_INDEX_RANGE", 7: "SA_ERR_HIP",
+          8: "SA_ERR_SPLITS"}
+SA_ERR_INDEX_RANGE = 6
 
 
 class SaDims(ctypes.Structure):
@@ -52,10 +56,14 @@ def lib():
         D = ctypes.POINTER(SaDims)
         L.sparse_attn_plan_splits.argtypes = [D]
         L.sparse_attn_plan_splits.restype = I32
-        L.sparse_attn_workspace_bytes.argtypes = [D, I32]
+        L.sparse_attn_workspace_bytes.argtypes = [D]
         L.sparse_attn_workspace_bytes.restype = SZ
-        L.sparse_attn_fwd.argtypes = [P, P, P, P, F, P, D, I32, P, SZ, P]
+        L.sparse_attn_workspace_bytes_splits.argtypes = [D, I32]
+        L.sparse_attn_workspace_bytes_splits.restype = SZ
+        L.sparse_attn_fwd.argtypes = [P, P, P, P, F, P, D, P, SZ, P]
         L.sparse_attn_fwd.restype = ctypes.c_int
+        L.sparse_attn_fwd_splits.argtypes = [P, P, P, P, F, P, D, I32, P, SZ, P]
+        L.sparse_attn_fwd_splits.restype = ctypes.c_int
         L.sparse_attn_fwd_rope.argtypes = [P, P, P, P, F, P, I32, P, D, I32, P, SZ, P]
         L.sparse_attn_fwd_rope.restype = ctypes.c_int
         L.sparse_attn_fwd_2src.argtypes = [P, P, I32, P, I32, I32, P, P, F, P, D, I32, P, SZ, P]

@@ -74,31 +74,52 @@ def plan_kernel(q, kv, idxs, num_splits: int = 0) -> str:
 
 
 def workspace_bytes(q, kv, idxs, num_splits: int = 0) -> int:
+    """sparse_attn_workspace_bytes (num_splits 0: the planned count) or
+    sparse_attn_workspace_bytes_splits."""
+    L = _lib.lib()
     with torch.cuda.device(q.device):
-        return int(_lib.lib().sparse_attn_workspace_bytes(ctypes.byref(_dims(q, kv, idxs)),
-                                                          num_splits))
+        dims = ctypes.byref(_dims(q, kv, idxs))
+        if num_splits == 0:
+            return int(L.sparse_attn_workspace_bytes(dims))
+        return int(L.sparse_attn_workspace_bytes_splits(dims, num_splits))
 
 
 def sparse_attn(q, kv, sink, idxs, scale: float, out=None, num_splits: int = 0,
-                workspace=None):
+                workspace=None, checked: bool = False):
     """o[b,t,h] = softmax over {sink_h} U {scale <q[b,t,h], kv[b,j]> : j in idxs[b,t], j >= 0}
-    applied to the rows kv[b,j] (the sink carries no value).  Returns bf16 [B,T,H,D]."""
+    applied to the rows kv[b,j] (the sink carries no value).  Returns bf16 [B,T,H,D].
+
+    num_splits 0 calls sparse_attn_fwd with the planned split count (the
+    workspace it needs is allocated here when none is given); 1..64 call
+    sparse_attn_fwd_splits.  checked=True first counts list entries >= N on
+    the device (sparse_attn_check_idxs, which synchronises to read the count)
+    and raises SA_ERR_INDEX_RANGE when there is one."""
     _check_tensors(q, kv, sink, idxs)
     dims = _dims(q, kv, idxs)
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if checked and check_idxs(idxs, kv.shape[1]) > 0:
+        _lib.check(_lib.SA_ERR_INDEX_RANGE, "sparse_attn (checked)")
     L = _lib.lib()
     with torch.cuda.device(q.device):
-        need = int(L.sparse_attn_workspace_bytes(ctypes.byref(dims), num_splits))
+        need = workspace_bytes(q, kv, idxs, num_splits)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        rc = L.sparse_attn_fwd(_ptr(q), _ptr(kv), _ptr(sink), _ptr(idxs), ctypes.c_float(scale),
-                               _ptr(out), ctypes.byref(dims), num_splits, _ptr(workspace),
-                               ws_bytes, _stream(q.device))
-    _lib.check(rc, "sparse_attn_fwd")
+        if num_splits == 0:
+            rc = L.sparse_attn_fwd(_ptr(q), _ptr(kv), _ptr(sink), _ptr(idxs),
+                                   ctypes.c_float(scale), _ptr(out), ctypes.byref(dims),
+                                   _ptr(workspace), ws_bytes, _stream(q.device))
+            what = "sparse_attn_fwd"
+        else:
+            rc = L.sparse_attn_fwd_splits(_ptr(q), _ptr(kv), _ptr(sink), _ptr(idxs),
+                                          ctypes.c_float(scale), _ptr(out), ctypes.byref(dims),
+                                          num_splits, _ptr(workspace), ws_bytes,
+                                          _stream(q.device))
+            what = "sparse_attn_fwd_splits"
+    _lib.check(rc, what)
     return out
 
 
@@ -122,7 +143,7 @@ def sparse_attn_rope(q, kv, sink, idxs, scale: float, freqs, rd: int, out=None,
         raise ValueError("out must be a contiguous bf16 tensor shaped like q")
     L = _lib.lib()
     with torch.cuda.device(q.device):
-        need = int(L.sparse_attn_workspace_bytes(ctypes.byref(dims), num_splits))
+        need = int(L.sparse_attn_workspace_bytes_splits(ctypes.byref(dims), num_splits))
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -150,7 +171,7 @@ def sparse_attn_2src(q, kv_win, kv_cmp, W: int, N: int, sink, idxs, scale: float
         out = torch.empty_like(q)
     L = _lib.lib()
     with torch.cuda.device(q.device):
-        need = int(L.sparse_attn_workspace_bytes(ctypes.byref(dims), num_splits))
+        need = int(L.sparse_attn_workspace_bytes_splits(ctypes.byref(dims), num_splits))
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -187,7 +208,7 @@ def sparse_attn_2src_fp4(q, kv_win, cmp_records, W: int, N: int, sink, idxs, sca
         out = torch.empty_like(q)
     L = _lib.lib()
     with torch.cuda.device(q.device):
-        need = int(L.sparse_attn_workspace_bytes(ctypes.byref(dims), num_splits))
+        need = int(L.sparse_attn_workspace_bytes_splits(ctypes.byref(dims), num_splits))
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

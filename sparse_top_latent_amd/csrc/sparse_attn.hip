@@ -88,6 +88,7 @@ struct FwdParams {
     float *ws_m;       // [Q, S, H] running max, log2 units
     float *ws_l;       // [Q, S, H] denominator relative to ws_m
     float *ws_x;       // [Q, S, H] power-of-two scale of each row of ws_o
+    int32_t *ws_plan;  // [Q] splits each query's list was cut into (written by split 0)
     int64_t N;
     int32_t T, H, K;
     int32_t S, HG, units, per_xcd, bs;  // see unit_of
@@ -122,6 +123,20 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// a10: the split plan of one query, from its own count of valid entries.
+// A launch provides S split slots per query (S chosen on the host from the
+// list capacity K); a query with n valid entries uses the first
+// Sq = ceil(n S / K) of them (1 <= Sq <= S), each taking a contiguous range
+// of about n / Sq valid entries.  No range is longer than with the capacity
+// plan, short lists leave their spare slots idle, and the combine merges only
+// Sq partials.  Computed on the device by every workgroup of the query after
+// compaction; split 0 records Sq for the combine.
+__device__ __forceinline__ int query_splits(int n, int K, int S) {
+    if (S <= 1 || K <= 0) return 1;
+    const int sq = (int)(((int64_t)n * S + K - 1) / K);
+    return sq < 1 ? 1 : (sq > S ? S : sq);
+}
 
 // Workgroup -> unit (one (query, head group, split) each), or -1 for a spare
 // workgroup.  Workgroups go to the eight XCDs round-robin by blockIdx; XCD x
@@ -683,8 +698,14 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 
     // a1: decode and compact the list, then take this split's slice.
     const int n = compact_list<NT>(raw, p.K, p.N, list, cnt);
-    const int lo = (n * s) / p.S;  // n <= LIST_CAP and s < MAX_SPLITS: no overflow
-    const int hi = (n * (s + 1)) / p.S;
+    const int Sq = query_splits(n, p.K, p.S);  // a10
+    if (p.S > 1 && s == 0 && hg == 0 && tid == 0) p.ws_plan[qi] = Sq;
+    if (s >= Sq) {  // a spare split slot: nothing to do once the early rows have landed
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+    }
+    const int lo = (n * s) / Sq;  // n <= LIST_CAP and s < MAX_SPLITS: no overflow
+    const int hi = (n * (s + 1)) / Sq;
     const int nchunks = (hi - lo + KC - 1) / KC;
 
     // Tail slots repeat the chunk's first row; their scores are masked to
@@ -1015,8 +1036,11 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 
     // a1: decode and compact the list (in place), then take this split's slice.
     const int n = compact_list<NT>((const LDS_AS int32_t *)list, p.K, p.N, list, cnt);
-    const int lo = (n * s) / p.S;  // n <= LIST_CAP and s < MAX_SPLITS: no overflow
-    const int hi = (n * (s + 1)) / p.S;
+    const int Sq = query_splits(n, p.K, p.S);  // a10
+    if (p.S > 1 && s == 0 && hg == 0 && tid == 0) p.ws_plan[qi] = Sq;
+    if (s >= Sq) return;  // a spare split slot
+    const int lo = (n * s) / Sq;  // n <= LIST_CAP and s < MAX_SPLITS: no overflow
+    const int hi = (n * (s + 1)) / Sq;
     const int nchunks = (hi - lo + KC - 1) / KC;
 
     // a2: chunk c (KC rows) into ring slot c % NB, one row per DMA
@@ -1240,6 +1264,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                                                       const float *__restrict__ ws_m,
                                                       const float *__restrict__ ws_l,
                                                       const float *__restrict__ ws_x,
+                                                      const int32_t *__restrict__ ws_plan,
                                                       const float *__restrict__ sink,
                                                       uint16_t *__restrict__ out, int64_t QH,
                                                       int H, int S, int per_xcd,
@@ -1265,6 +1290,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     const int h = ok ? (int)(qh % H) : 0;
     const int c8 = sl * 8;
     const int64_t slot0 = qi * S * H + h;    // slot of split j: slot0 + j * H
+    // a10: the splits this query's list was cut into (the first Sq slots)
+    int Sq = ok ? ws_plan[qi] : 1;
+    Sq = Sq < 1 ? 1 : (Sq > S ? S : Sq);
 
     // The partials are read once: non-temporal loads with up to four splits
     // (measured faster there; with eight, ordinary loads were faster).
@@ -1274,7 +1302,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     };
     u32x4_t v[SB];
 #pragma unroll
-    for (int j = 0; j < SB; ++j) v[j] = ok && j < S ? part(j) : u32x4_t{0, 0, 0, 0};
+    for (int j = 0; j < SB; ++j) v[j] = ok && j < Sq ? part(j) : u32x4_t{0, 0, 0, 0};
     // rotary dims: the (cos, sin) of the lane's four pairs
     const bool rot = ok && c8 >= D - rd;
     float4 cs0 = {1.f, 0.f, 1.f, 0.f}, cs1 = cs0;
@@ -1288,7 +1316,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
         const int j = sl + k * LPR;
-        const bool has = ok && j < S;
+        const bool has = ok && j < Sq;
         const int64_t slot = slot0 + (int64_t)j * H;
         mj[k] = has ? ws_m[slot] : -INFINITY;
         lj[k] = has ? ws_l[slot] : 0.f;
@@ -1324,7 +1352,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         if (j0 > 0) {
 #pragma unroll
             for (int j = 0; j < SB; ++j)
-                v[j] = ok && j0 + j < S ? part(j0 + j) : u32x4_t{0, 0, 0, 0};
+                v[j] = ok && j0 + j < Sq ? part(j0 + j) : u32x4_t{0, 0, 0, 0};
         }
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
@@ -1710,11 +1738,11 @@ int head_groups(const sa_dims *d, int S) {
 }
 
 struct WsLayout {
-    size_t o_off, m_off, l_off, x_off, bytes;
+    size_t o_off, m_off, l_off, x_off, plan_off, bytes;
 };
 
 WsLayout ws_layout(const sa_dims *d, int S) {
-    WsLayout w{0, 0, 0, 0, 0};
+    WsLayout w{0, 0, 0, 0, 0, 0};
     if (S <= 1) return w;
     const size_t slots = (size_t)queries(d) * S * d->H;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -1722,7 +1750,8 @@ WsLayout ws_layout(const sa_dims *d, int S) {
     w.m_off = up(slots * d->D * sizeof(uint16_t));
     w.l_off = w.m_off + up(slots * sizeof(float));
     w.x_off = w.l_off + up(slots * sizeof(float));
-    w.bytes = w.x_off + up(slots * sizeof(float));
+    w.plan_off = w.x_off + up(slots * sizeof(float));
+    w.bytes = w.plan_off + up((size_t)queries(d) * sizeof(int32_t));
     return w;
 }
 
@@ -1791,11 +1820,12 @@ hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
     const float *wm = (const float *)((const uint8_t *)ws + L.m_off);
     const float *wl = (const float *)((const uint8_t *)ws + L.l_off);
     const float *wx = (const float *)((const uint8_t *)ws + L.x_off);
+    const int32_t *wp = (const int32_t *)((const uint8_t *)ws + L.plan_off);
     uint16_t *o = (uint16_t *)out;
     switch (d->D) {
-        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
-        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
-        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
+        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
+        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
+        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
     }
     return hipGetLastError();
 }
@@ -1849,6 +1879,7 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
         p.ws_m = (float *)((uint8_t *)ws + L.m_off);
         p.ws_l = (float *)((uint8_t *)ws + L.l_off);
         p.ws_x = (float *)((uint8_t *)ws + L.x_off);
+        p.ws_plan = (int32_t *)((uint8_t *)ws + L.plan_off);
     }
     p.N = d->N;
     p.T = d->T;
@@ -1923,7 +1954,7 @@ int32_t sparse_attn_plan_splits(const sa_dims *d) {
     return plan_splits(d);
 }
 
-size_t sparse_attn_workspace_bytes(const sa_dims *d, int32_t num_splits) {
+size_t sparse_attn_workspace_bytes_splits(const sa_dims *d, int32_t num_splits) {
     if (check_dims(d) != SA_OK || num_splits < 0 || num_splits > MAX_SPLITS) return 0;
     int S = num_splits;
     if (S == 0) {
@@ -1933,11 +1964,22 @@ size_t sparse_attn_workspace_bytes(const sa_dims *d, int32_t num_splits) {
     return ws_layout(d, S).bytes;
 }
 
-int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int32_t *idxs,
-                    float scale, void *out, const sa_dims *d, int32_t num_splits, void *workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
+size_t sparse_attn_workspace_bytes(const sa_dims *d) {
+    return sparse_attn_workspace_bytes_splits(d, 0);
+}
+
+int sparse_attn_fwd_splits(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                           float scale, void *out, const sa_dims *d, int32_t num_splits,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return sparse_attn_fwd_rope(q, kv, sink, idxs, scale, nullptr, 0, out, d, num_splits,
                                 workspace, workspace_bytes, stream);
+}
+
+int sparse_attn_fwd(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                    float scale, void *out, const sa_dims *d, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+    return sparse_attn_fwd_rope(q, kv, sink, idxs, scale, nullptr, 0, out, d, 0, workspace,
+                                workspace_bytes, stream);
 }
 
 int sparse_attn_fwd_rope(const void *q, const void *kv, const float *sink, const int32_t *idxs,
@@ -2139,8 +2181,9 @@ const char *sparse_attn_status_str(int status) {
         case SA_ERR_UNSUPPORTED: return "unsupported size (D must be 128, 256 or 512; K <= 2048)";
         case SA_ERR_ALIGN: return "misaligned pointer (q/kv/out 16 B, idxs/sink 4 B, workspace 256 B)";
         case SA_ERR_WORKSPACE: return "workspace missing or too small";
-        case SA_ERR_SPLITS: return "num_splits out of range";
+        case SA_ERR_INDEX_RANGE: return "an index list holds an entry >= N (checked mode)";
         case SA_ERR_HIP: return "HIP error";
+        case SA_ERR_SPLITS: return "num_splits out of range";
         default: return "unknown status";
     }
 }

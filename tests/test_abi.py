@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
 
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN, SA_ERR_WORKSPACE, \
-    SA_ERR_SPLITS, SA_ERR_HIP = range(8)
+    SA_ERR_INDEX_RANGE, SA_ERR_HIP, SA_ERR_SPLITS = range(9)
 
 # fake device addresses: never dereferenced, because every call below fails its
 # argument checks first
@@ -35,10 +35,42 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     assert set(names) == set(_lib.SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
+
+
+def declared_signature(name):
+    """Parameter types and names of a declaration in the header, whitespace folded."""
+    text = open(HEADER).read()
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    return [" ".join(p.split()) for p in m.group(1).split(",")]
+
+
+def test_boundary_signatures_as_documented():
+    # the page's call sparse_attn(q, kv, attn_sink, topk_idxs, softmax_scale)
+    # with out, the dims, a workspace and the stream made explicit
+    assert declared_signature("sparse_attn_fwd") == [
+        "const void *q", "const void *kv", "const float *sink", "const int32_t *idxs",
+        "float scale", "void *out", "const sa_dims *d", "void *workspace",
+        "size_t workspace_bytes", "hipStream_t stream"]
+    assert declared_signature("sparse_attn_workspace_bytes") == ["const sa_dims *d"]
+    assert declared_signature("sparse_attn_fwd_splits") == [
+        "const void *q", "const void *kv", "const float *sink", "const int32_t *idxs",
+        "float scale", "void *out", "const sa_dims *d", "int32_t num_splits", "void *workspace",
+        "size_t workspace_bytes", "hipStream_t stream"]
+    assert declared_signature("sparse_attn_workspace_bytes_splits") == [
+        "const sa_dims *d", "int32_t num_splits"]
+    assert declared_signature("sparse_attn_check_idxs") == [
+        "const int32_t *idxs", "const sa_dims *d", "int32_t *d_bad_count", "hipStream_t stream"]
+    assert declared_signature("sparse_attn_status_str") == ["int status"]
+    text = open(HEADER).read()
+    for i, name in enumerate(["SA_OK", "SA_ERR_NULL", "SA_ERR_SHAPE", "SA_ERR_UNSUPPORTED",
+                              "SA_ERR_ALIGN", "SA_ERR_WORKSPACE", "SA_ERR_INDEX_RANGE",
+                              "SA_ERR_HIP", "SA_ERR_SPLITS"]):
+        assert re.search(r"\b%s = %d\b" % (name, i), text), name
 
 
 def dims(B=2, T=3, H=64, D=512, N=100, K=40):
@@ -46,13 +78,18 @@ def dims(B=2, T=3, H=64, D=512, N=100, K=40):
 
 
 def fwd(L, q=A, kv=A, sink=None, idxs=A, out=A2, d=None, S=1, ws=None, wsb=0):
+    return L.sparse_attn_fwd_splits(q, kv, sink, idxs, ctypes.c_float(0.1), out,
+                                    dims() if d is None else d, S, ws, wsb, None)
+
+
+def fwd_planned(L, q=A, kv=A, sink=None, idxs=A, out=A2, d=None, ws=None, wsb=0):
     return L.sparse_attn_fwd(q, kv, sink, idxs, ctypes.c_float(0.1), out,
-                             dims() if d is None else d, S, ws, wsb, None)
+                             dims() if d is None else d, ws, wsb, None)
 
 
 def test_status_strings(L):
     seen = set()
-    for rc in range(8):
+    for rc in range(9):
         s = _lib.status_str(rc)
         assert s and s not in seen
         seen.add(s)
@@ -101,16 +138,28 @@ def test_split_and_workspace_errors(L):
 def test_zero_queries_is_a_noop(L):
     assert fwd(L, q=None, kv=None, idxs=None, out=None, d=dims(B=0)) == SA_OK
     assert fwd(L, q=None, kv=None, idxs=None, out=None, d=dims(T=0)) == SA_OK
+    assert fwd_planned(L, q=None, kv=None, idxs=None, out=None, d=dims(B=0)) == SA_OK
+
+
+def test_planned_entry_point_argument_errors(L):
+    # one split without a workspace: argument errors come back before any HIP call
+    assert fwd_planned(L, d=ctypes.POINTER(SaDims)()) == SA_ERR_NULL
+    assert fwd_planned(L, d=dims(D=100)) == SA_ERR_UNSUPPORTED
+    assert fwd_planned(L, q=None) == SA_ERR_NULL
+    assert fwd_planned(L, out=MIS) == SA_ERR_ALIGN
+    assert fwd_planned(L, d=dims(H=0)) == SA_ERR_SHAPE
 
 
 def test_workspace_size_formula(L):
     B, T, H, D, S = 3, 5, 64, 512, 4
-    got = L.sparse_attn_workspace_bytes(dims(B=B, T=T, H=H, D=D), S)
+    got = L.sparse_attn_workspace_bytes_splits(dims(B=B, T=T, H=H, D=D), S)
     up = lambda x: (x + 255) // 256 * 256
     slots = B * T * S * H
-    assert got == up(slots * D * 2) + 2 * up(slots * 4) + up(slots * 8)
-    assert L.sparse_attn_workspace_bytes(dims(), 1) == 0
-    assert L.sparse_attn_workspace_bytes(dims(D=100), 2) == 0
+    assert got == up(slots * D * 2) + 3 * up(slots * 4) + up(B * T * 4)
+    assert L.sparse_attn_workspace_bytes_splits(dims(), 1) == 0
+    assert L.sparse_attn_workspace_bytes_splits(dims(D=100), 2) == 0
+    assert L.sparse_attn_workspace_bytes_splits(dims(), 65) == 0
+    assert L.sparse_attn_workspace_bytes(dims(D=100)) == 0
 
 
 def test_check_idxs_errors(L):

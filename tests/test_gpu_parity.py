@@ -128,7 +128,7 @@ def test_large_norm_queries(ref):
 
 def test_large_magnitude_rows_on_the_split_path(ref):
     # rows ~2^20: a split's partial output would overflow fp16 without the
-    # per-half-row power-of-two scale
+    # per-row power-of-two scale
     import copy
     w = copy.deepcopy(wl.make_random(15, 2, 2, 64, 512, 300, 200, p_unused=0.1))
     w.vals = [wl.to_bf16_bits(wl.bf16_bits_to_f32(v) * np.float32(2.0 ** 20)) for v in w.vals]
@@ -141,6 +141,36 @@ def test_large_magnitude_rows_on_the_split_path(ref):
         got = run_gpu(w, S, q_bits=q_small)
         # the output is linear in the rows: compare at the unscaled magnitude
         assert_close(got * 2.0 ** -20, exp * 2.0 ** -20, f"rows x 2^20 S={S}")
+
+
+def test_small_magnitude_rows_on_the_split_path(ref):
+    # rows ~2^-20: a split's partial output would sink into fp16 subnormals
+    # (or flush to zero) unless each row is scaled up by its power of two
+    import copy
+    w = copy.deepcopy(wl.make_random(16, 2, 2, 64, 512, 300, 200, p_unused=0.1))
+    w.vals = [wl.to_bf16_bits(wl.bf16_bits_to_f32(v) * np.float32(2.0 ** -20)) for v in w.vals]
+    q_big = wl.to_bf16_bits(wl.bf16_bits_to_f32(w.q) * np.float32(2.0 ** 20))
+    exp = ref(q_big, w.kv_host(), w.sink, w.idxs, w.scale)
+    assert np.abs(exp).max() < 2.0 ** -14   # fp16 subnormal range without the scale
+    for S in (1, 2, 3):
+        got = run_gpu(w, S, q_bits=q_big)
+        # the output is linear in the rows: compare at the unscaled magnitude
+        assert_close(got * 2.0 ** 20, exp * 2.0 ** 20, f"rows x 2^-20 S={S}")
+
+
+def test_sink_minus_infinity(ref):
+    # a sink of -inf removes the sink from the softmax; with no valid entry as
+    # well there is nothing to attend to and the output is 0 (never NaN), on
+    # the one-split path as on the split path
+    w = wl.make_random(17, 2, 2, 64, 512, 60, 8, p_unused=0.0)
+    ninf = np.full(64, -np.inf, np.float32)
+    one = np.full((2, 2, 8), -1, np.int32)
+    one[..., 3] = w.idxs[..., 3]
+    for S in (1, 2):
+        got = run_gpu(w, S, np.full((2, 2, 8), -1, np.int32), ninf)
+        assert np.all(got == 0), f"all unused, sink -inf, S={S}"
+        check(ref, w, S, idxs=one, sink=ninf, what=f"one entry, sink -inf, S={S}")
+        check(ref, w, S, sink=ninf, what=f"full lists, sink -inf, S={S}")
 
 
 def test_permuted_lists_and_scattered_unused(ref):
@@ -630,25 +660,55 @@ def test_full_config_every_query(ref, name):
         sampled_check(ref, w, [(b, 0) for b in range(w.B)], got)
 
 
-def test_full_prefill_sampled(ref):
+def compact_rows(w):
+    """Each sequence's stored rows as a compact kv [B, R, D] (R = the most rows
+    any sequence stores) and its lists remapped onto them by position among the
+    sorted stored rows.  Exact plumbing, no arithmetic: it keeps the 8.6 GB
+    dense key-value tensor of the ragged batch out of host memory."""
+    R = max(len(r) for r in w.rows)
+    kv = np.full((w.B, R, w.D), wl.BF16_NAN, np.uint16)
+    idx = np.full_like(w.idxs, -1)
+    for b in range(w.B):
+        kv[b, :len(w.rows[b])] = w.vals[b]
+        m = w.idxs[b] >= 0
+        idx[b][m] = np.searchsorted(w.rows[b], w.idxs[b][m])
+    return kv, idx
+
+
+def test_full_prefill_every_query(ref):
+    """All 4096 prefill queries (the many-query kernel at its real launch
+    shape, every unit and the spare workgroups of the last XCD turn) against
+    the oracle, element by element."""
     w = wl.make("prefill")
     got = run_gpu(w, 0)
-    assert np.isfinite(got).all()
-    rng = np.random.default_rng(0)
-    ts = sorted(set([0, 1, 2, 126, 127, 128, 129, 1023, 2048, 4094, 4095]
-                    + list(rng.choice(4096, 37, replace=False))))
-    sampled_check(ref, w, [(0, int(t)) for t in ts], got)
+    exp = ref(w.q, w.kv_host(), w.sink, w.idxs, w.scale)
+    assert_close(got, exp, "prefill, every query")
 
 
-def test_full_ragged_sampled(ref):
+@pytest.mark.parametrize("S", [0, 2])
+def test_full_ragged_every_query(ref, S):
+    """All 256 ragged-batch queries against the oracle, in the planned launch
+    (one split) and with two split slots per query, where each query's own
+    valid count decides how many it uses."""
     w = wl.make("ragged")
-    got = run_gpu(w, 0)
-    assert np.isfinite(got).all()
-    valid = (w.idxs >= 0).sum(-1)[:, 0]
-    order = np.argsort(valid)
-    pick = sorted(set(list(order[:16]) + list(order[-16:]) +
-                      list(np.random.default_rng(1).choice(256, 32, replace=False))))
-    sampled_check(ref, w, [(int(b), 0) for b in pick], got)
+    got = run_gpu(w, S)
+    kvc, idc = compact_rows(w)
+    exp = ref(w.q, kvc, w.sink, idc, w.scale)
+    assert_close(got, exp, f"ragged S={S}, every query")
+
+
+@pytest.mark.parametrize("S", [3, 4, 8])
+def test_per_query_split_plan(ref, S):
+    """Lists of very different valid counts in one launch: each query cuts its
+    own valid entries into ceil(n S / K) ranges (spare split slots idle, the
+    combine merges only the ranges used), including empty and one-entry lists."""
+    w = wl.make_decode(B=10)
+    lst = w.idxs.copy()
+    for b, n in enumerate([0, 1, 31, 64, 100, 161, 320, 500, 639, 640]):
+        keep = np.zeros(w.K, bool)
+        keep[np.random.default_rng(b).choice(w.K, n, replace=False)] = True
+        lst[b, 0][~keep] = -1
+    check(ref, w, S, idxs=lst, what=f"per-query plan S={S}")
 
 
 def test_full_decode_with_unused_entries_in_every_slice(ref):
