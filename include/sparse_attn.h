@@ -176,6 +176,28 @@ int sparse_attn_fwd_2src_fp4(const void *q, const void *kv_win, int32_t win_rows
                              const sa_dims *d, int32_t num_splits, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sparse_attn_fwd_splits with the split workspace taken from a static device
+ * array of the library instead of a caller's buffer.  The array holds
+ * sparse_attn_noalloc_max_bytes() bytes (33 MiB, enough for every planned split
+ * count) on each device the library runs on, from when the library is loaded
+ * until the process ends; its address is looked up once per device on the
+ * first call there.  num_splits 0 = planned, else 1..64; a split count whose
+ * workspace (sparse_attn_workspace_bytes_splits) exceeds the array returns
+ * SA_ERR_WORKSPACE.  The call allocates nothing (no hipMalloc, no library
+ * allocation) and only enqueues on `stream`.  Every call on one device shares
+ * that device's array, which keeps the last call's partials: calls that can
+ * overlap on one device (other streams, other threads) race and must be
+ * serialised by the caller.  Other arguments, checks and results as
+ * sparse_attn_fwd_splits. */
+int sparse_attn_fwd_noalloc(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                            float scale, void *out, const sa_dims *d, int32_t num_splits,
+                            hipStream_t stream);
+
+/* Bytes of the static array sparse_attn_fwd_noalloc uses. */
+size_t sparse_attn_noalloc_max_bytes(void);
+
 /* First half of the split path (num_splits >= 2): writes the partials of every
  * split into `workspace` and nothing into out.  Same arguments and checks as
  * sparse_attn_fwd_splits, without out. */

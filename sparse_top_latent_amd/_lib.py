@@ -17,6 +17,8 @@ SYMBOLS = (
     "sparse_attn_workspace_bytes_splits",
     "sparse_attn_fwd",
     "sparse_attn_fwd_splits",
+    "sparse_attn_fwd_noalloc",
+    "sparse_attn_noalloc_max_bytes",
     "sparse_attn_fwd_rope",
     "sparse_attn_fwd_2src",
     "sparse_attn_fwd_2src_fp4",
@@ -64,6 +66,10 @@ def lib():
         L.sparse_attn_fwd.restype = ctypes.c_int
         L.sparse_attn_fwd_splits.argtypes = [P, P, P, P, F, P, D, I32, P, SZ, P]
         L.sparse_attn_fwd_splits.restype = ctypes.c_int
+        L.sparse_attn_fwd_noalloc.argtypes = [P, P, P, P, F, P, D, I32, P]
+        L.sparse_attn_fwd_noalloc.restype = ctypes.c_int
+        L.sparse_attn_noalloc_max_bytes.argtypes = []
+        L.sparse_attn_noalloc_max_bytes.restype = SZ
         L.sparse_attn_fwd_rope.argtypes = [P, P, P, P, F, P, I32, P, D, I32, P, SZ, P]
         L.sparse_attn_fwd_rope.restype = ctypes.c_int
         L.sparse_attn_fwd_2src.argtypes = [P, P, I32, P, I32, I32, P, P, F, P, D, I32, P, SZ, P]

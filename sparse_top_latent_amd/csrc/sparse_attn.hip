@@ -2044,6 +2044,32 @@ int fwd_two_source(const void *q, const void *kv_win, int32_t win_rows, const vo
 // bytes of one FP4 record: D/2 code bytes + D/16 scale bytes, padded to 16
 int32_t fp4_record_bytes(int32_t D) { return (9 * D / 16 + 15) / 16 * 16; }
 
+// Workspace of sparse_attn_fwd_noalloc: a static device array (one copy on
+// every device the library runs on, held until the process ends).  33 MiB
+// covers every planned split count: a split is only planned when the
+// workgroups of one split do not fill the device, and then S workgroups per
+// query stay below twice the compute units, i.e. under 2 * 256 * 64 partial
+// rows of 1 KB at D = 512 plus their scalars and plan.
+constexpr size_t SCRATCH_BYTES = (size_t)33 << 20;
+__device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept: in host code
+// the array's name is not a device address.  nullptr if the lookup fails.
+void *scratch_device_ptr() {
+    static std::mutex mu;
+    static void *ptr[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -2070,6 +2096,30 @@ int sparse_attn_fwd_2src_fp4(const void *q, const void *kv_win, int32_t win_rows
                           sparse_attn_fp4_record_bytes(d->D), sink, idxs, scale, out, d,
                           num_splits, workspace, workspace_bytes, stream);
 }
+
+int sparse_attn_fwd_noalloc(const void *q, const void *kv, const float *sink, const int32_t *idxs,
+                            float scale, void *out, const sa_dims *d, int32_t num_splits,
+                            hipStream_t stream) {
+    int rc = check_dims(d);
+    if (rc != SA_OK) return rc;
+    if (num_splits < 0 || num_splits > MAX_SPLITS) return SA_ERR_SPLITS;
+    if (queries(d) == 0) return SA_OK;
+    int S = num_splits;
+    if (S == 0) {
+        S = plan_splits(d);
+        if (S < 0) return -S;
+    }
+    if (ws_layout(d, S).bytes > SCRATCH_BYTES) return SA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (S > 1) {
+        ws = scratch_device_ptr();
+        if (ws == nullptr) return SA_ERR_HIP;
+    }
+    return sparse_attn_fwd_rope(q, kv, sink, idxs, scale, nullptr, 0, out, d, S, ws,
+                                S > 1 ? SCRATCH_BYTES : 0, stream);
+}
+
+size_t sparse_attn_noalloc_max_bytes(void) { return SCRATCH_BYTES; }
 
 int sparse_attn_fwd_partial(const void *q, const void *kv, const int32_t *idxs, float scale,
                             const sa_dims *d, int32_t num_splits, void *workspace,

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     assert set(names) == set(_lib.SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -256,3 +256,17 @@ def test_topk_argument_errors(L):
     assert t(Q=0, out=None, scores=None) == SA_OK            # nothing to do
     assert t(k=0, out=None) == SA_OK
     assert L.sparse_attn_topk(A, None, 1, 2**31 - 5, 10, 100, A2, 10, None) == SA_ERR_SHAPE
+
+
+def test_noalloc_argument_errors(L):
+    # all rejected before any HIP call
+    noalloc = lambda d, S=0, q=A: L.sparse_attn_fwd_noalloc(q, A, None, A, ctypes.c_float(0.1), A2,
+                                                            d, S, None)
+    assert noalloc(ctypes.POINTER(SaDims)()) == SA_ERR_NULL
+    assert noalloc(dims(D=100)) == SA_ERR_UNSUPPORTED
+    assert noalloc(dims(), S=65) == SA_ERR_SPLITS
+    assert noalloc(dims(), S=-1) == SA_ERR_SPLITS
+    assert noalloc(dims(B=0)) == SA_OK
+    assert noalloc(dims(B=512, T=1, K=640), S=64) == SA_ERR_WORKSPACE
+    assert L.sparse_attn_noalloc_max_bytes() == 33 << 20
+
