@@ -1,9 +1,12 @@
 #!/usr/bin/env python3
 """Throughput of the sparse latent attention step on one MI355X.
 
-Workload: the DeepSeek-V4.1 decode batch (B=64 sequences, one query each,
-H=64 heads of width 512, K=640 list entries = 128 window rows + 512 distinct
-compressed rows out of 8192, scale 512^-0.5), synthetic and seeded.
+Headline workload: the DeepSeek-V4.1 decode batch (B=64 sequences, one query
+each, H=64 heads of width 512, K=640 list entries = 128 window rows + 512
+distinct compressed rows out of 8192, scale 512^-0.5), synthetic and seeded.
+The same JSON line also carries the other configurations (causal prefill of
+4096 queries, long-context decode, the ragged batch and window-only lists)
+under ``workloads``, each timed the same way.
 
 A step is one pass of the whole path over the batch: index decode, gather,
 QK^T, sink softmax, PV and (with splits) the log-sum-exp combine.  Inputs are
@@ -13,7 +16,7 @@ not still sitting in the 256 MB Infinity Cache from the previous step (a
 second, labelled figure runs with one copy).  Each step is replayed from a
 captured HIP graph so that host launch overhead is not part of the time.
 
-Prints one JSON line.  ``value`` = queries per second.
+Prints one JSON line.  ``value`` = queries per second of the headline workload.
 """
 from __future__ import annotations
 
@@ -57,7 +60,12 @@ def parse():
                          "segment (decode and causal prefill shapes) and decode top-k + attention")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run plain 256 MiB copies first (HBM counter calibration)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="time only the headline workload (profiling runs)")
     return ap.parse_args()
+
+
+OTHER_WORKLOADS = ("prefill", "long", "ragged", "window")
 
 
 def source_digest():
@@ -65,11 +73,9 @@ def source_digest():
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
 
 
-def read_counters(workload):
-    """HBM bytes per launch of the main kernel from the committed rocprofv3
-    counter summary of this workload, if it was taken on the current kernel
-    source."""
-    path = os.path.join(PROFILES, f"attn_fwd_{workload}_counters.txt")
+def _read_kv(path):
+    """key: value lines of a committed counter summary, or None when it is
+    missing or was taken on another kernel source."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -79,8 +85,30 @@ def read_counters(workload):
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256_16") != source_digest():
         return None
+    return kv
+
+
+def read_counters(workload):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload."""
+    kv = _read_kv(os.path.join(PROFILES, f"attn_fwd_{workload}_counters.txt"))
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return None if kv is None else float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def read_mfma_busy(workload):
+    """MFMA busy share per SIMD of the dominant kernel from the committed
+    rocprofv3 SQ counter summary of this workload: SQ_VALU_MFMA_BUSY_CYCLES /
+    (4 SIMDs x SQ_BUSY_CU_CYCLES), with the clock those counters imply."""
+    kv = _read_kv(os.path.join(PROFILES, f"attn_fwd_{workload}_sq_counters.txt"))
+    try:
+        if kv is None:
+            return None
+        return {"mfma_busy_per_simd": float(kv["mfma_busy_per_simd"]),
+                "clock_ghz": float(kv["clock_ghz"]),
+                "source": f"profiles/attn_fwd_{workload}_sq_counters.txt"}
     except (KeyError, ValueError):
         return None
 
@@ -109,137 +137,166 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    cap_stream = torch.cuda.Stream()
+
+    def measure(w, R, warm_cache):
+        """Time one workload: ms per step (graph of R steps over R input
+        copies), optionally with one copy (warm cache), and the dominant
+        kernel alone on the stream it runs on.  Returns the figures and the
+        device inputs."""
+        q0 = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+        kv0 = w.kv_device(dev)
+        idx0 = torch.from_numpy(w.idxs).to(dev)
+        sink = torch.from_numpy(w.sink).to(dev)
+        qs = [q0] + [q0.clone() for _ in range(R - 1)]
+        kvs = [kv0] + [kv0.clone() for _ in range(R - 1)]
+        idxs = [idx0] + [idx0.clone() for _ in range(R - 1)]
+        out = torch.empty_like(q0)
+        S = args.splits if args.splits > 0 else api.plan_splits(q0, kv0, idx0)
+        kernel = api.plan_kernel(q0, kv0, idx0, S)
+        ws_bytes = api.workspace_bytes(q0, kv0, idx0, S)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            api.sparse_attn(qs[i], kvs[i], sink, idxs[i], w.scale, out=out, num_splits=S,
+                            workspace=ws)
+
+        # Warm up eagerly (also checks that the path runs), then capture
+        # graphs: one holding R consecutive steps (one per input copy, as a
+        # model's decode graph would chain them) and one graph per single step
+        # for a remainder.
+        for i in range(max(1, args.warmup)):
+            step(i % R)
+        torch.cuda.synchronize()
+
+        def capture(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                for i in copies:
+                    step(i)
+            return g
+
+        g_rot = capture(range(R))
+        g_one = [capture([i]) for i in range(R)]
+        g_warm = capture([0] * R) if warm_cache else None
+        for g in [g_rot] + g_one + ([g_warm] if g_warm is not None else []):
+            g.replay()
+        torch.cuda.synchronize()
+
+        def timed(g_many):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            gate(torch)
+            e0.record()
+            for _ in range(args.steps // R):
+                g_many.replay()
+            for k in range(args.steps % R):
+                g_one[k if g_many is g_rot else 0].replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+
+        ms_step = timed(g_rot)
+        ms_step_warm = timed(g_warm) if g_warm is not None else None
+
+        # the dominant kernel alone: back-to-back launches on the stream it
+        # runs on (torch's current stream, where the binding launches)
+        stream = torch.cuda.current_stream(dev)
+        torch.cuda.synchronize()
+        gate(torch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(args.steps):
+            i = k % R
+            if S > 1:
+                api.sparse_attn_partial(qs[i], kvs[i], idxs[i], w.scale, S, ws)
+            else:
+                api.sparse_attn(qs[i], kvs[i], sink, idxs[i], w.scale, out=out, num_splits=1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_main = e0.elapsed_time(e1) / args.steps
+
+        Qn = w.queries
+        valid = w.valid_entries()
+        kv_bytes = w.distinct_rows() * w.D * 2
+        q_bytes = Qn * w.H * w.D * 2
+        idx_bytes = w.idxs.size * 4
+        # algorithmic bytes of the dominant kernel: rows, q and lists in; with
+        # one split also the bf16 output and the sink (else those belong to
+        # the combine)
+        main_bytes = (kv_bytes + q_bytes + idx_bytes + (q_bytes if S == 1 else 0)
+                      + (w.H * 4 if S == 1 else 0))
+        path_bytes = w.algorithmic_bytes()
+        flops = w.algorithmic_flops()
+        t_step = ms_step * 1e-3
+        t_roof = max(path_bytes / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+        t_main = ms_main * 1e-3
+        if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > path_bytes / (HBM_PEAK_GBPS * 1e9):
+            roof = {"kernel": kernel, "bound": "mfma",
+                    "achieved": round(flops / t_main / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s",
+                    "frac": round(flops / t_main / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "algorithmic_flops_per_launch": flops}
+        else:
+            roof = {"kernel": kernel, "bound": "hbm",
+                    "achieved": round(main_bytes / t_main / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(main_bytes / t_main / 1e9 / HBM_PEAK_GBPS, 4),
+                    "algorithmic_bytes_per_launch": main_bytes}
+        roof["traffic"] = read_counters(w.name)
+        roof["avg_launch_us"] = round(ms_main * 1e3, 3)
+        roof["mfma_busy_counters"] = read_mfma_busy(w.name)
+        fig = {
+            "ms_per_step": round(ms_step, 5),
+            "value": round(Qn / t_step, 1),
+            "config": {"workload": f"deepseek-v4.1-{w.name}", "B": w.B, "T": w.T, "H": w.H,
+                       "D": w.D, "K": w.K, "N": w.N, "valid_entries": valid, "splits": S,
+                       "input_copies_rotated": R},
+            "gathered_kv_GBps": round(valid * w.D * 2 / t_step / 1e9, 1),
+            "path_roofline_frac": round(t_roof / t_step, 4),
+            "mfma_util": round(flops / t_step / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+            "roofline": roof,
+        }
+        if ms_step_warm is not None:
+            fig["warm_cache"] = {
+                "value": round(Qn / (ms_step_warm * 1e-3), 1),
+                "ms_per_step": round(ms_step_warm, 5),
+                "note": "same inputs every step: rows may be served from the Infinity Cache"}
+        state = {"qs": qs, "kvs": kvs, "idxs": idxs, "sink": sink, "out": out, "ws": ws, "S": S,
+                 "step": step}
+        return fig, state
+
     w = wl.make(args.workload)
     R = max(1, args.rotate)
-    q0 = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
-    kv0 = w.kv_device(dev)
-    idx0 = torch.from_numpy(w.idxs).to(dev)
-    sink = torch.from_numpy(w.sink).to(dev)
-    qs = [q0] + [q0.clone() for _ in range(R - 1)]
-    kvs = [kv0] + [kv0.clone() for _ in range(R - 1)]
-    idxs = [idx0] + [idx0.clone() for _ in range(R - 1)]
-    out = torch.empty_like(q0)
-    S = args.splits if args.splits > 0 else api.plan_splits(q0, kv0, idx0)
-    kernel = api.plan_kernel(q0, kv0, idx0, S)
-    ws_bytes = api.workspace_bytes(q0, kv0, idx0, S)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-
+    fig, st = measure(w, R, warm_cache=True)
+    qs, kvs, idxs, sink, out, ws, S, step = (st[k] for k in ("qs", "kvs", "idxs", "sink", "out",
+                                                            "ws", "S", "step"))
+    Qn = w.queries
+    flops = w.algorithmic_flops()
     if args.copy_probe:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
-
-    def step(i):
-        api.sparse_attn(qs[i], kvs[i], sink, idxs[i], w.scale, out=out, num_splits=S,
-                        workspace=ws)
-
-    # Warm up eagerly (also checks that the path runs), then capture graphs:
-    # one holding R consecutive steps (one per input copy, as a model's decode
-    # graph would chain them) and one graph per single step for a remainder.
-    for i in range(args.warmup):
-        step(i % R)
-    torch.cuda.synchronize()
-    cap_stream = torch.cuda.Stream()
-
-    def capture(copies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap_stream):
-            for i in copies:
-                step(i)
-        return g
-
-    g_rot = capture(range(R))
-    g_one = [capture([i]) for i in range(R)]
-    g_warm = capture([0] * R)
-    for g in [g_rot, g_warm] + g_one:
-        g.replay()
-    torch.cuda.synchronize()
-
-    def timed(g_many):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        gate(torch)
-        e0.record()
-        for _ in range(args.steps // R):
-            g_many.replay()
-        for k in range(args.steps % R):
-            g_one[k if g_many is g_rot else 0].replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    ms_step = timed(g_rot)
-    ms_step_warm = timed(g_warm)
-
-    # the dominant kernel alone: back-to-back launches on the stream it runs on
-    stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-    gate(torch)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for k in range(args.steps):
-        i = k % R
-        if S > 1:
-            api.sparse_attn_partial(qs[i], kvs[i], idxs[i], w.scale, S, ws)
-        else:
-            api.sparse_attn(qs[i], kvs[i], sink, idxs[i], w.scale, out=out, num_splits=1)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_main = e0.elapsed_time(e1) / args.steps
-
-    # figures
-    Qn = w.queries
-    valid = w.valid_entries()
-    kv_bytes = w.distinct_rows() * w.D * 2
-    q_bytes = Qn * w.H * w.D * 2
-    idx_bytes = w.idxs.size * 4
-    # algorithmic bytes of the main kernel: rows, q and lists in; with one
-    # split also the bf16 output and the sink (else those belong to combine)
-    main_bytes = kv_bytes + q_bytes + idx_bytes + (q_bytes if S == 1 else 0) + (w.H * 4 if S == 1 else 0)
-    path_bytes = w.algorithmic_bytes()
-    flops = w.algorithmic_flops()
-    t_step = ms_step * 1e-3
-    t_hbm = path_bytes / (HBM_PEAK_GBPS * 1e9)
-    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-    t_roof = max(t_hbm, t_mfma)
-    t_main = ms_main * 1e-3
-    if t_mfma > t_hbm:
-        roof = {"kernel": kernel, "bound": "mfma",
-                "achieved": round(flops / t_main / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(flops / t_main / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                "algorithmic_flops_per_launch": flops}
-    else:
-        roof = {"kernel": kernel, "bound": "hbm",
-                "achieved": round(main_bytes / t_main / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(main_bytes / t_main / 1e9 / HBM_PEAK_GBPS, 4),
-                "algorithmic_bytes_per_launch": main_bytes}
-    roof["traffic"] = read_counters(w.name)
-    roof["avg_launch_us"] = round(ms_main * 1e3, 3)
     line = {
         "metric": "sparse-attn queries/sec + gathered-KV HBM GB/s (% roofline), H=64 D=512 K=640",
-        "value": round(Qn / t_step, 1),
+        "value": fig["value"],
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": fig["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"deepseek-v4.1-{w.name}", "B": w.B, "T": w.T, "H": w.H,
-                   "D": w.D, "K": w.K, "N": w.N, "valid_entries": valid, "splits": S,
-                   "input_copies_rotated": R, "parallelism": "single-gpu"},
-        "gathered_kv_GBps": round(valid * w.D * 2 / t_step / 1e9, 1),
-        "path_roofline_frac": round(t_roof / t_step, 4),
-        "mfma_util": round(flops / t_step / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
-        "warm_cache": {"value": round(Qn / (ms_step_warm * 1e-3), 1),
-                       "ms_per_step": round(ms_step_warm, 5),
-                       "note": "same inputs every step: rows may be served from the Infinity Cache"},
-        "roofline": roof,
+        "config": dict(fig["config"], parallelism="single-gpu"),
+        "gathered_kv_GBps": fig["gathered_kv_GBps"],
+        "path_roofline_frac": fig["path_roofline_frac"],
+        "mfma_util": fig["mfma_util"],
+        "warm_cache": fig["warm_cache"],
+        "roofline": fig["roofline"],
     }
 
     def time_graph(fn):
@@ -373,21 +430,77 @@ def main():
                                             "value": round(Qn / (ms_kd * 1e-3), 1)}
         line["topk"] = res
 
+    if not args.no_workloads and args.workload == "decode":
+        # the other configurations, each timed like the headline (a step =
+        # the whole path over its batch); kernels and rooflines per workload
+        res = {}
+        for name in OTHER_WORKLOADS:
+            wo = wl.make(name)
+            fo, so = measure(wo, R, warm_cache=False)
+            res[name] = {k: fo[k] for k in ("value", "ms_per_step", "gathered_kv_GBps",
+                                             "path_roofline_frac", "mfma_util", "roofline")}
+            res[name]["unit"] = "queries/s"
+            res[name]["config"] = fo["config"]
+            del so, fo, wo
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        line["workloads"] = res
+
     if not args.no_cpu_baseline:
+        import ctypes
         import oracle
         kvh = np.stack([w.kv_dense_host(b) for b in range(w.B)])
-        done, t0 = 0, time.perf_counter()
-        while True:
-            oracle.sparse_attn_ref(w.q, kvh, w.sink, w.idxs, w.scale)
-            done += 1
-            el = time.perf_counter() - t0
-            if el >= 10.0 or done >= 1000:
-                break
+
+        def rate(fn, n_per_call, budget):
+            done, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                done += 1
+                el = time.perf_counter() - t0
+                if el >= budget or done >= 1000:
+                    return done * n_per_call / el, done, el
+
+        # all the host cores the process may use (OpenMP over queries)
+        v_all, done, el = rate(lambda: oracle.sparse_attn_ref(w.q, kvh, w.sink, w.idxs, w.scale),
+                               Qn, 10.0)
+        threads = oracle.num_threads()
+        # one thread on a fixed subset (the first 8 queries): the per-core rate
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        try:
+            v_one, done1, el1 = rate(lambda: oracle.sparse_attn_ref(
+                w.q[:8], kvh[:8], w.sink, w.idxs[:8], w.scale), 8, 3.0)
+        finally:
+            gomp.omp_set_num_threads(threads)
+        cpu_model = "unknown"
+        try:
+            for ln in open("/proc/cpuinfo"):
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         line["cpu_baseline"] = {
-            "value": round(done * Qn / el, 2), "unit": "queries/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "value": round(v_all, 2), "unit": "queries/s",
+            "cores": threads, "kind": "oracle",
             "sample": f"the full {w.name} batch ({Qn} queries) computed {done} times "
-                      f"by the fp64 oracle, {el:.1f} s wall"}
+                      f"by the fp64 oracle, {el:.1f} s wall",
+            "cpu_model": cpu_model,
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "per_core": {"value": round(v_one, 2), "unit": "queries/s", "threads": 1,
+                         "sample": f"queries 0..7 of the {w.name} batch, {done1} times, "
+                                   f"{el1:.1f} s wall"}}
+        if not args.no_workloads and args.workload == "decode":
+            # prefill: a stratified subset (every 64th query t, 64 queries)
+            wp = wl.make("prefill")
+            ts = np.arange(0, wp.T, 64)
+            kvp = wp.kv_host()
+            v_p, donep, elp = rate(lambda: oracle.sparse_attn_ref(
+                wp.q[:, ts], kvp, wp.sink, wp.idxs[:, ts], wp.scale), len(ts), 3.0)
+            line["cpu_baseline"]["prefill"] = {
+                "value": round(v_p, 2), "unit": "queries/s", "threads": threads,
+                "sample": f"every 64th prefill query ({len(ts)} queries, t = 0, 64, ..., "
+                          f"{ts[-1]}), {donep} times, {elp:.1f} s wall"}
     print(json.dumps(line), flush=True)
 
 
