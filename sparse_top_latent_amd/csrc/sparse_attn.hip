@@ -325,6 +325,21 @@ __device__ __forceinline__ void wait_vm_ahead(int ahead) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// s_waitcnt until at most n (0 <= n <= MAXN <= 16) vector memory operations
+// of this wave are outstanding, n known only at run time (the immediate must
+// be a constant): one branch per possible value.
+template <int MAXN>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+    static_assert(MAXN >= 0 && MAXN <= 16, "a few cases");
+#define SA_WAIT_CASE(k) \
+    if (MAXN >= k && n == k) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(k) : "memory"); return; }
+    SA_WAIT_CASE(16) SA_WAIT_CASE(15) SA_WAIT_CASE(14) SA_WAIT_CASE(13) SA_WAIT_CASE(12)
+    SA_WAIT_CASE(11) SA_WAIT_CASE(10) SA_WAIT_CASE(9) SA_WAIT_CASE(8) SA_WAIT_CASE(7)
+    SA_WAIT_CASE(6) SA_WAIT_CASE(5) SA_WAIT_CASE(4) SA_WAIT_CASE(3) SA_WAIT_CASE(2) SA_WAIT_CASE(1)
+#undef SA_WAIT_CASE
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // a7 / a8: epilogue shared by the attention kernels.  The workgroup holds
 // HWG = 16*NTL heads; wave w of NW holds the output columns
 // w*DW .. w*DW + DW - 1 (DW = D/NW) of every head: lane (li, g) holds
@@ -471,8 +486,10 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 // groups of 16 elements, E2M1 codes with one E4M3 scale per group).  A record
 // holds D/2 bytes of codes (byte k: element 2k in the low nibble, 2k + 1 in
 // the high one) and then D/16 scale bytes, padded to `rec` bytes.  Each
-// record lands by LDS-DMA in the last `rec` bytes of its padded ring row (RS
-// bytes); this pass rewrites those rows in place as bf16 (element i =
+// record lands by LDS-DMA in its padded ring row (RS bytes): in the last `rec`
+// bytes of an even row, in the first `rec` bytes of an odd one, so that the
+// records of rows 2i and 2i + 1 are adjacent and one DMA instruction fetches
+// both.  This pass rewrites those rows in place as bf16 (element i =
 // E2M1(code i) * E4M3(scale i/16), exact in bf16: 2 and 4 significant bits).
 // All codes are read before any row is written, since the bf16 row covers
 // the record.  Rows whose list entry is below W hold bf16 already.
@@ -483,7 +500,6 @@ __device__ void expand_fp4(LDS_AS uint8_t *T, int RS, int rec, const int32_t *li
     constexpr int ITEMS = KCH * G;
     constexpr int PER = (ITEMS + NT - 1) / NT;
     const int tid = threadIdx.x;
-    const int off = RS - rec;
     u32x2_t codes[PER];
     uint32_t sc[PER];
     bool on[PER];
@@ -496,7 +512,7 @@ __device__ void expand_fp4(LDS_AS uint8_t *T, int RS, int rec, const int32_t *li
         codes[k] = u32x2_t{0u, 0u};
         sc[k] = 0u;
         if (on[k]) {
-            const LDS_AS uint8_t *src = T + r * RS + off;
+            const LDS_AS uint8_t *src = T + r * RS + ((r & 1) ? 0 : RS - rec);
             codes[k] = *(const LDS_AS u32x2_t *)(src + 8 * g);
             sc[k] = src[D / 2 + g];
         }
@@ -638,9 +654,11 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     // A wave takes IPW consecutive entries of the chunk (its k-th is entry
     // wid*IPW + k, at that position of the slot), so that four of its rows
     // sit within reach of one instruction's offset.  Each wave instruction
-    // moves one row: lane l < D/8 fetches its 16 bytes and lands at byte 16*l
-    // of the row's padded slot (an FP4 record, FP4 build and rows >= W: lanes
-    // < rec2/16, at the tail of the slot).
+    // moves one bf16 row: lane l < D/8 fetches its 16 bytes and lands at byte
+    // 16*l of the row's padded slot.  FP4 build, rows >= W: an FP4 record
+    // (rec2/16 lanes) lands at the tail of an even row and at the head of an
+    // odd one, so a pair of records shares one instruction (see expand_fp4).
+    // The lambdas return the number of DMA instructions they issued.
     static_assert(IPW % 4 == 0, "rows are requested four at a time");
     auto dma_row = [&](int c, int k, int rw) {
         LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (wid * IPW + k) * RS;
@@ -648,22 +666,34 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             if (CPR == 64 || lane < CPR)
                 lds_dma16_nt((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8, (LDS_AS void *)dst);
         } else if (lane * 16 < p.rec2) {
-            lds_dma16_nt(recb + (int64_t)rw * p.rec2 + lane * 16, (LDS_AS void *)(dst + RS - p.rec2));
+            lds_dma16_nt(recb + (int64_t)rw * p.rec2 + lane * 16,
+                         (LDS_AS void *)(dst + ((k & 1) ? 0 : RS - p.rec2)));
         }
+        return 1;
+    };
+    // FP4 build: rows k (even) and k + 1; two records in one instruction
+    auto dma_pair = [&](int c, int k, int r0, int r1) {
+        if (r0 >= p.W && r1 >= p.W) {
+            const int nl = p.rec2 / 16;  // lanes per record
+            LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (wid * IPW + k) * RS + RS - p.rec2;
+            const uint8_t *src = lane < nl ? recb + (int64_t)r0 * p.rec2 + lane * 16
+                                           : recb + (int64_t)r1 * p.rec2 + (lane - nl) * 16;
+            if (lane < 2 * nl) lds_dma16_nt(src, (LDS_AS void *)dst);
+            return 1;
+        }
+        return dma_row(c, k, r0) + dma_row(c, k + 1, r1);
     };
     // the wave's rows k0 .. k0+3 of chunk c (bf16 rows: one M0 write)
     auto dma_quad = [&](int c, int k0, int r0, int r1, int r2, int r3) {
         if constexpr (FP4) {
-            dma_row(c, k0, r0);
-            dma_row(c, k0 + 1, r1);
-            dma_row(c, k0 + 2, r2);
-            dma_row(c, k0 + 3, r3);
+            return dma_pair(c, k0, r0, r1) + dma_pair(c, k0 + 2, r2, r3);
         } else {
             LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (wid * IPW + k0) * RS;
             auto src = [&](int rw) {
                 return (const uint8_t *)((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8);
             };
             if (CPR == 64 || lane < CPR) lds_dma16x4_nt<RS>(src(r0), src(r1), src(r2), src(r3), dst);
+            return 4;
         }
     };
 
@@ -815,14 +845,23 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     };
     // the wave's rows 4q .. 4q+3 of chunk cc, from the lanes of `rows`
     auto quad_from = [&](int cc, int q, int rows) {
-        dma_quad(cc, 4 * q, __builtin_amdgcn_readlane(rows, 4 * q), __builtin_amdgcn_readlane(rows, 4 * q + 1),
-                 __builtin_amdgcn_readlane(rows, 4 * q + 2), __builtin_amdgcn_readlane(rows, 4 * q + 3));
+        return dma_quad(cc, 4 * q, __builtin_amdgcn_readlane(rows, 4 * q),
+                        __builtin_amdgcn_readlane(rows, 4 * q + 1),
+                        __builtin_amdgcn_readlane(rows, 4 * q + 2),
+                        __builtin_amdgcn_readlane(rows, 4 * q + 3));
     };
     int next_rows = 1 < nchunks ? rows_of(1) : 0;   // the chunk requested next
     int next2_rows = 2 < nchunks ? rows_of(2) : 0;  // chunk 2, during chunk 0
+    // DMA instructions this wave issued for the chunk after the current one
+    // (FP4 build: pairs of records share one, so the count varies)
+    int issued_ahead = 0;
     for (int c = 0; c < nchunks; ++c) {
         // chunk c has landed once at most the chunk after it is pending
-        wait_vm_ahead<IPW, 1>(min(1, nchunks - 1 - c));
+        if constexpr (FP4) {
+            wait_vm_upto<IPW>(c + 1 < nchunks ? issued_ahead : 0);
+        } else {
+            wait_vm_ahead<IPW, 1>(min(1, nchunks - 1 - c));
+        }
         __syncthreads();
         // PV of chunk c - 1 (its weights were published before this barrier)
         if (c > 0) pv_chunk(c - 1);
@@ -842,6 +881,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         // operand i, and the scheduling barriers keep that order (left alone,
         // the scheduler requests each operand next to its MFMA and the LDS
         // latency is exposed on every one).
+        int issued_now = 0;  // DMA instructions of the last chunk requested below
         f32x4_t sacc[2][HT];
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
@@ -871,17 +911,18 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
                     for (int q = 0; q < NG; ++q)
                         if (i == dma_step(q, NG, NQK)) {
                             if (q < NG / 2) quad_from(1, q, next_rows);
-                            else quad_from(2, q - NG / 2, next2_rows);
+                            else issued_now += quad_from(2, q - NG / 2, next2_rows);
                         }
                 } else if (do_stage) {
                     constexpr int NG = IPW / 4;
 #pragma unroll
                     for (int q = 0; q < NG; ++q)
-                        if (i == dma_step(q, NG, NQK)) quad_from(rq, q, next_rows);
+                        if (i == dma_step(q, NG, NQK)) issued_now += quad_from(rq, q, next_rows);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if (two || do_stage) issued_ahead = issued_now;
         if (c + 3 < nchunks) next_rows = rows_of(c + 3);
         // the pair adds its two halves (a + b == b + a, so both waves agree)
 #pragma unroll
@@ -1064,14 +1105,29 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
             const uint16_t *src = (row < p.W ? kva : kvb2) + (int64_t)row * D;
             if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, dst);
         } else if (lane * 16 < p.rec2) {
-            lds_dma16_s(recb + (int64_t)row * p.rec2, lane * 16, dst + RS - p.rec2);
+            // an FP4 record: at the tail of an even row, the head of an odd one
+            lds_dma16_s(recb + (int64_t)row * p.rec2, lane * 16, dst + ((k & 1) ? 0 : RS - p.rec2));
+        }
+    };
+    // FP4 build: rows k (even) and k + 1; two records share one instruction
+    auto stage_pair = [&](int c, int rows, int k) {
+        const int r0 = __builtin_amdgcn_readlane(rows, k), r1 = __builtin_amdgcn_readlane(rows, k + 1);
+        if (r0 >= p.W && r1 >= p.W) {
+            const int nl = p.rec2 / 16;  // lanes per record
+            LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NB][0] + (wid * IPW + k) * RS + RS - p.rec2;
+            const uint8_t *src = lane < nl ? recb + (int64_t)r0 * p.rec2 + lane * 16
+                                           : recb + (int64_t)r1 * p.rec2 + (lane - nl) * 16;
+            if (lane < 2 * nl) lds_dma16_nt(src, (LDS_AS void *)dst);
+        } else {
+            stage_one(c, rows, k);
+            stage_one(c, rows, k + 1);
         }
     };
     // rows 4q .. 4q+3 (bf16 rows: one M0 write)
     auto stage_quad = [&](int c, int rows, int q) {
         if constexpr (FP4) {
-#pragma unroll
-            for (int k = 4 * q; k < 4 * q + 4; ++k) stage_one(c, rows, k);
+            stage_pair(c, rows, 4 * q);
+            stage_pair(c, rows, 4 * q + 2);
         } else {
             auto src = [&](int k) {
                 const int row = __builtin_amdgcn_readlane(rows, k);
