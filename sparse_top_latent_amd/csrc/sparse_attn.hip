@@ -796,15 +796,14 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     // is requested right after the MFMAs of pair u).
     auto pv_chunk = [&](int cc) {
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[cc % NBUF][0];
+        // every tile's weights and factor and the first V operands are
+        // requested before any is used (one LDS round trip, not one per tile)
         bf16x8_t pb[NTL];
+        float al[NTL];
 #pragma unroll
         for (int t = 0; t < NTL; ++t) {
             pb[t] = __builtin_bit_cast(bf16x8_t, pbuf[t][lane]);
-            const float a = abuf[t][li];
-            if (__ballot(a != 1.f)) {
-#pragma unroll
-                for (int u = 0; u < NU; ++u) o[t][u] *= a;
-            }
+            al[t] = abuf[t][li];
         }
         constexpr int PVP = NU < 4 ? NU : 4;
         const int r0 = 4 * g + (li >> 2);
@@ -819,6 +818,15 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         bf16x8_t va[PVP];
 #pragma unroll
         for (int u = 0; u < PVP; ++u) va[u] = vload(u);
+        bool scaled = false;
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) scaled |= al[t] != 1.f;
+        if (__ballot(scaled)) {  // a running max moved (rare): rescale
+#pragma unroll
+            for (int t = 0; t < NTL; ++t)
+#pragma unroll
+                for (int u = 0; u < NU; ++u) o[t][u] *= al[t];
+        }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
 #pragma unroll
@@ -1215,10 +1223,15 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 
         // a5: online softmax of the own tile (lazy max, as in attn_fwd_kernel)
         float sv[8];
+        if (cnt_c == KC) {  // a full chunk: nothing to mask (uniform branch)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = 16 * (e >> 2) + 4 * g + (e & 3);
-            sv[e] = cnt_c == KC || j < cnt_c ? sacc[e >> 2][e & 3] * p.qk_scale_log2 : -INFINITY;
+            for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3] * p.qk_scale_log2;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = 16 * (e >> 2) + 4 * g + (e & 3);
+                sv[e] = j < cnt_c ? sacc[e >> 2][e & 3] * p.qk_scale_log2 : -INFINITY;
+            }
         }
         const float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                                  fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
@@ -1245,24 +1258,24 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         xp[wid][lane] = pw;
         if (g == 0) xa[wid][li] = alpha;
         __syncthreads();
-        bf16x8_t pb[NTL];
-#pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-            pb[t] = __builtin_bit_cast(bf16x8_t, t == wid ? pw : xp[t][lane]);
-            const float a = xa[t][li];
-            if (__ballot(a != 1.f)) {
-#pragma unroll
-                for (int u = 0; u < NU; ++u) o[t][u] *= a;
-            }
-        }
 
         // a6: O^T[d, h] += V^T[d, j] P^T[j, h] over this wave's columns; the
         // transpose loads hand lane (li, g) column 16u + li of rows 4g..4g+3
         // and 16+4g..16+4g+3, the k-slots of its weights
         // (pipelined by hand like QK^T: transpose pair u + PVP is loaded right
-        // after the MFMAs of pair u)
+        // after the MFMAs of pair u).  Every tile's weights and factor and the
+        // first V operands are requested before any is used, so the LDS
+        // latency is paid once (a branch on each factor as it arrives would
+        // serialise the round trips).
         {
             constexpr int PVP = NU < 3 ? NU : 3;
+            bf16x8_t pb[NTL];
+            float al[NTL];
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) {
+                pb[t] = __builtin_bit_cast(bf16x8_t, xp[t][lane]);
+                al[t] = xa[t][li];
+            }
             const LDS_AS uint8_t *R0 = T + (4 * g + (li >> 2)) * RS + (li & 3) * 8;
             const LDS_AS uint8_t *R1 = R0 + 16 * RS;
             auto vload = [&](int u) {
@@ -1274,6 +1287,15 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
             bf16x8_t va[PVP];
 #pragma unroll
             for (int u = 0; u < PVP; ++u) va[u] = vload(u);
+            bool scaled = false;
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) scaled |= al[t] != 1.f;
+            if (__ballot(scaled)) {  // a running max moved (rare): rescale
+#pragma unroll
+                for (int t = 0; t < NTL; ++t)
+#pragma unroll
+                    for (int u = 0; u < NU; ++u) o[t][u] *= al[t];
+            }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
 #pragma unroll
