@@ -79,7 +79,7 @@ struct FwdParams {
     const uint16_t *kv2;    // second source [B, rows_b, D]
     int64_t W, rows_a, rows_b;
     int32_t rec2;           // 0: the second source holds bf16 rows; else it holds FP4
-                            // records of rec2 bytes (see expand_fp4)
+                            // records of rec2 bytes (see expand_fp4_own)
     const float *sink;
     const int32_t *idxs;
     uint16_t *out;     // non-split path
@@ -489,24 +489,28 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 // record lands by LDS-DMA in its padded ring row (RS bytes): in the last `rec`
 // bytes of an even row, in the first `rec` bytes of an odd one, so that the
 // records of rows 2i and 2i + 1 are adjacent and one DMA instruction fetches
-// both.  This pass rewrites those rows in place as bf16 (element i =
-// E2M1(code i) * E4M3(scale i/16), exact in bf16: 2 and 4 significant bits).
-// All codes are read before any row is written, since the bf16 row covers
-// the record.  Rows whose list entry is below W hold bf16 already.
-template <int D, int NT, int KCH>
-__device__ void expand_fp4(LDS_AS uint8_t *T, int RS, int rec, const int32_t *list, int e0, int hi,
-                           int64_t W) {
+// both.  Each wave rewrites the ring rows it requested itself (rows
+// wid*IPW .. wid*IPW + IPW - 1 of the chunk) in place as bf16 once its own
+// requests have landed (element i = E2M1(code i) * E4M3(scale i/16), exact in
+// bf16: 2 and 4 significant bits): no other wave writes those rows, so the
+// wave reads every record of its rows into registers before it writes any
+// bf16 row (a bf16 row covers its record), and the chunk's barrier publishes
+// them; the expansion needs no barrier of its own.  Rows whose list entry is
+// below W hold bf16 already.
+template <int D, int IPW>
+__device__ __forceinline__ void expand_fp4_own(LDS_AS uint8_t *T, int RS, int rec, const int32_t *list,
+                                               int e0, int hi, int64_t W) {
     constexpr int G = D / 16;  // groups (and scale bytes) per row
-    constexpr int ITEMS = KCH * G;
-    constexpr int PER = (ITEMS + NT - 1) / NT;
-    const int tid = threadIdx.x;
+    constexpr int ITEMS = IPW * G;
+    constexpr int PER = (ITEMS + 63) / 64;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     u32x2_t codes[PER];
     uint32_t sc[PER];
     bool on[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        const int i = k * NT + tid;
-        const int r = i / G, g = i % G;
+        const int i = k * 64 + lane;
+        const int r = wid * IPW + i / G, g = i % G;
         const int e = e0 + r;
         on[k] = i < ITEMS && list[e < hi ? e : e0] >= W;
         codes[k] = u32x2_t{0u, 0u};
@@ -517,16 +521,12 @@ __device__ void expand_fp4(LDS_AS uint8_t *T, int RS, int rec, const int32_t *li
             sc[k] = src[D / 2 + g];
         }
     }
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         if (on[k]) {
-            const int i = k * NT + tid;
-            const int r = i / G, g = i % G;
+            const int i = k * 64 + lane;
+            const int r = wid * IPW + i / G, g = i % G;
             const float s = e4m3_to_f32(sc[k]);
-            // byte j of the group holds elements 2j, 2j + 1.  Scale 1: exact
-            // E2M1 values (the instruction applies only the power of two of its
-            // scale, so the E4M3 scale is a separate multiply).
             const uint32_t c0 = codes[k][0], c1 = codes[k][1];
             const f32x2_t f[8] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 0),
                                   __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 1),
@@ -544,7 +544,6 @@ __device__ void expand_fp4(LDS_AS uint8_t *T, int RS, int rec, const int32_t *li
             *(LDS_AS u32x4_t *)(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
         }
     }
-    __syncthreads();
 }
 
 // Work split: a workgroup holds NHQ groups of 16*HT heads; each group is
@@ -657,7 +656,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     // moves one bf16 row: lane l < D/8 fetches its 16 bytes and lands at byte
     // 16*l of the row's padded slot.  FP4 build, rows >= W: an FP4 record
     // (rec2/16 lanes) lands at the tail of an even row and at the head of an
-    // odd one, so a pair of records shares one instruction (see expand_fp4).
+    // odd one, so a pair of records shares one instruction (see expand_fp4_own).
     // The lambdas return the number of DMA instructions they issued.
     static_assert(IPW % 4 == 0, "rows are requested four at a time");
     auto dma_row = [&](int c, int k, int rw) {
@@ -867,6 +866,9 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         // chunk c has landed once at most the chunk after it is pending
         if constexpr (FP4) {
             wait_vm_upto<IPW>(c + 1 < nchunks ? issued_ahead : 0);
+            // this wave's FP4 records of chunk c have landed: expand them
+            expand_fp4_own<D, IPW>((LDS_AS uint8_t *)&tile[c % NBUF][0], RS, p.rec2, list,
+                                   lo + c * KC, hi, p.W);
         } else {
             wait_vm_ahead<IPW, 1>(min(1, nchunks - 1 - c));
         }
@@ -881,7 +883,6 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NBUF][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
-        if (FP4) expand_fp4<D, NT, KC>((LDS_AS uint8_t *)T, RS, p.rec2, list, lo + c * KC, hi, p.W);
 
         // a4: partial S^T[j, h] over this wave's half of d (two 16-row tiles
         // x HT head tiles; each K operand feeds HT MFMAs).  Software-pipelined
@@ -1180,6 +1181,9 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         // landed; otherwise it would wait for q's loads inside the MFMA
         // sequence, which also drains the next chunk's DMAs issued there.
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // FP4 build: this wave's records of chunk c have landed; expand them
+        if (FP4) expand_fp4_own<D, IPW>((LDS_AS uint8_t *)&tile[c % NB][0], RS, p.rec2, list, lo + c * KC,
+                                        hi, p.W);
         __syncthreads();
         // chunk c + 1 goes into the slot chunk c - 1 left; its DMAs are spread
         // through the QK^T MFMAs below, so that a wave never waits for a burst
@@ -1188,7 +1192,6 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 
         const LDS_AS uint8_t *T = (const LDS_AS uint8_t *)&tile[c % NB][0];
         const int cnt_c = min(KC, hi - (lo + c * KC));
-        if (FP4) expand_fp4<D, NT, KC>((LDS_AS uint8_t *)T, RS, p.rec2, list, lo + c * KC, hi, p.W);
 
         // a4: S^T[j, hown] over the whole of d, rows j = 16 jt + 4 g + i.
         // Software-pipelined by hand: operand load i + QKP is issued right
