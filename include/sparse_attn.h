@@ -73,9 +73,10 @@ enum sa_status {
 };
 
 /* Number of index-range splits the library picks when num_splits is 0: one
- * split when the queries alone fill the device, else enough splits (each at
- * least 64 list entries) to give every compute unit work.  Returns >= 1, or a
- * negative sa_status on bad dims or a failed device query. */
+ * split when the queries alone fill the device or when the head-split kernel
+ * serves the launch (see sparse_attn_fwd), else enough splits (each at least 64
+ * list entries) to give every compute unit work.  Returns >= 1, or a negative
+ * sa_status on bad dims or a failed device query. */
 int32_t sparse_attn_plan_splits(const sa_dims *d);
 
 /* Bytes of workspace sparse_attn_fwd needs for the split count the library
@@ -94,6 +95,12 @@ size_t sparse_attn_workspace_bytes_splits(const sa_dims *d, int32_t num_splits);
 
 /* The whole step: out = sparse_attn(q, kv, sink, idxs, scale), the call of the
  * pages' Attention.forward excerpt with the dims and a workspace made explicit.
+ * An unsplit launch at D = 512 with K <= 448 whose B*T*ceil(H/16) units all fit
+ * the device's compute units at once runs the head-split kernel: one workgroup
+ * per query and 16 heads over the whole list, no workspace; the planner then
+ * picks one split.  Its softmax weights are rounded to bf16 against a
+ * reference per block of 16 entries instead of per 32-entry chunk, so its
+ * results agree with the deep-gather kernel's to within that rounding.
  * workspace NULL: one split (always correct, no workspace).  Otherwise the
  * planned split count (sparse_attn_plan_splits), which needs
  * workspace_bytes >= sparse_attn_workspace_bytes(d), else SA_ERR_WORKSPACE.
@@ -239,8 +246,9 @@ int sparse_attn_check_idxs(const int32_t *idxs, const sa_dims *d, int32_t *d_bad
 
 /* Name of the attention kernel a call with these dims and num_splits (0 =
  * planned) launches on the current device, as profilers list it (static
- * text), or NULL on bad arguments or a failed device query.  Launches of at
- * least two workgroups per compute unit take the many-query kernel (two
+ * text), or NULL on bad arguments or a failed device query.  Unsplit launches
+ * the head-split kernel serves (see sparse_attn_fwd) take it; other launches
+ * of at least two workgroups per compute unit take the many-query kernel (two
  * workgroups share a unit); smaller ones the deep-gather kernel.  The name is
  * that of the bf16-rows build (sparse_attn_fwd_2src_fp4 runs the same kernel
  * built with FP4 records, <..., true>).  For profiling and reports; no call

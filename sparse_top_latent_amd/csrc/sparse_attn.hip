@@ -62,6 +62,12 @@ constexpr size_t fwd_static_lds(int D, int NHQ, int HT) {
            (size_t)NHQ * HT * 1024 + (size_t)NHQ * HT * 64 + (size_t)(2 * NHQ) * 4;
 }
 size_t list_lds_bytes(int K) { return ((size_t)(K > 0 ? K : 1) * 4 + 15) / 16 * 16; }
+// Static LDS of attn_fwd_hs_kernel<D>: three round buffers of 48 padded rows,
+// two sets of published weights (3 blocks x 64 lanes x 8 bytes) with their
+// references and sums, per-wave counts.
+constexpr size_t hs_static_lds(int D) {
+    return 3 * 48 * (size_t)(2 * D + 32) + 2 * 3 * 64 * 8 + 2 * 2 * 3 * 16 * 4 + 8 * 4;
+}
 constexpr int MAX_SPLITS = 64;
 constexpr float LOG2E = 1.4426950408889634f;
 // The running max is only raised when a chunk beats it by more than this many
@@ -1327,6 +1333,314 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     store_outputs<D, NW, NTL>(p, o, mh, lh, red, qi, s, hg, (LDS_AS uint8_t *)&tile[0][0]);
 }
 
+// Head-split variant, for unsplit launches whose (query, 16 heads) units all
+// fit the compute units at once and whose lists are short (decode steps with
+// few valid entries, window-only lists).  Same steps and results as
+// attn_fwd_kernel up to the rounding of the softmax reference; the work is
+// split the other way round: a workgroup serves 16 heads of one query over the
+// query's whole list, so no partials leave the workgroup and no combine runs,
+// at the price of every row being read by each of the query's head groups
+// (they share an XCD, so the repeats come from L2).
+//
+// FP4 build (f2): a row of the second source is its record (rec2 bytes, one
+// load by the first rec2/16 lanes), written into its padded LDS row where
+// expand_fp4_own expects it and expanded there in place by the wave that wrote
+// it, before the round's barrier; the bf16 rows the kernel then reads are the
+// ones the bf16 build reads, so both builds agree bit for bit.
+//
+// The list is consumed in rounds of RR = 48 entries.  Rows travel through
+// registers: each of the 8 waves loads RPW = 6 rows of round i + 2 (ordinary
+// 16-byte loads, the compiler tracks them) while round i is computed, and
+// writes round i into one of three LDS round buffers, so no LDS holds rows in
+// flight.  Iteration i: round i's rows go to LDS, one barrier, then
+//   - waves 0..2 (the scorers) each take one 16-row block of round i: S^T over
+//     all of d (q of the 16 heads in registers), the block's softmax weights
+//     as bf16, published with the block's reference max and weight sum;
+//   - every wave adds round i - 1's blocks to O^T for its D/8 output columns of
+//     all 16 heads (the published weights are the MFMA operands as written).
+// Three round buffers and two weight buffers keep each iteration's writers off
+// what the previous iteration's readers use, so one barrier per round does.
+//
+// a5 with per-block references: a scorer takes the running reference R (log2
+// units, identical in every wave) and raises its block's reference to the
+// block's max only when that beats R by more than MAX_SLACK, as the
+// deep-gather kernel does per chunk.  The column owners then move R to the
+// largest reference of the round (rescaling O and the denominator once) and
+// add each block with factor 2^(m_b - R), which is 1 unless a block raised
+// its reference; only then do the blocks go through a scaled path.
+template <int D, bool FP4>
+__global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
+    constexpr int NW = 8, NT = NW * 64;
+    constexpr int RR = 48;               // list entries per round
+    constexpr int RPW = RR / NW;         // rows each wave loads per round
+    constexpr int NB = RR / 16;          // 16-row blocks per round, one scorer wave each
+    constexpr int NBUF = 3;              // LDS round buffers
+    constexpr int RS = 2 * D + 32;       // padded LDS row (see attn_fwd_kernel)
+    constexpr int KS = D / 32;           // QK^T k-steps
+    constexpr int CW = D / NW;           // output columns per wave
+    constexpr int NTL = CW / 16;         // 16-column output tiles per wave
+    static_assert(D == 512, "one row per wave load instruction (64 lanes x 16 bytes)");
+    static_assert(RPW * NW == RR && NB * 16 == RR, "rounds split evenly");
+    __shared__ __attribute__((aligned(16))) uint8_t rbuf[NBUF][RR * RS];
+    __shared__ __attribute__((aligned(16))) u32x2_t pub[2][NB][64];  // bf16 weights per block
+    __shared__ float mbs[2][NB][16], lbs[2][NB][16];                 // reference and sum per head
+    __shared__ int32_t cnt[NW];
+    extern __shared__ int32_t list[];  // the compacted list (K entries, dynamic)
+    static_assert(sizeof(rbuf) + sizeof(pub) + sizeof(mbs) + sizeof(lbs) + sizeof(cnt) == hs_static_lds(D),
+                  "the host's LDS figure matches the declarations");
+
+    const int unit = unit_of(blockIdx.x, p.units, p.bs);
+    if (unit < 0) return;
+    const int hg = unit % p.HG;
+    const int qi = unit / p.HG;
+    const int b = qi / p.T;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int h = hg * 16 + li;  // head of this lane (QK^T columns, softmax, outputs)
+    const bool scorer = wid < NB;
+    const uint16_t *kva = p.kv + (int64_t)b * p.rows_a * D;
+    const uint16_t *kvb2 = p.kv2 + ((int64_t)b * p.rows_b - p.W) * D;
+    const uint8_t *recb = (const uint8_t *)p.kv2 + ((int64_t)b * p.rows_b - p.W) * p.rec2;
+    // a2: this lane's 16 bytes of row j (one wave instruction per row); FP4
+    // build, j >= W: of its record (lanes below rec2/16)
+    auto load_row = [&](int j, u32x4_t &dst) {
+        if (!FP4 || j < p.W)
+            dst = *((const u32x4_t *)((j < p.W ? kva : kvb2) + (int64_t)j * D) + lane);
+        else if (lane * 16 < p.rec2)
+            dst = *(const u32x4_t *)(recb + (int64_t)j * p.rec2 + lane * 16);
+    };
+    // row j into position r of a round buffer (a record where expand_fp4_own reads it)
+    auto write_row = [&](LDS_AS uint8_t *Lb, int r, int j, const u32x4_t &v) {
+        if (!FP4 || j < p.W)
+            *(LDS_AS u32x4_t *)(Lb + r * RS + lane * 16) = v;
+        else if (lane * 16 < p.rec2)
+            *(LDS_AS u32x4_t *)(Lb + r * RS + ((r & 1) ? 0 : RS - p.rec2) + lane * 16) = v;
+    };
+
+    // Prologue: the raw list and the 16 heads' q (into the last round buffer,
+    // untouched until round 2) by LDS-DMA; the scorers then take q into
+    // registers as the B operands of QK^T.
+    LDS_AS uint8_t *qlds = (LDS_AS uint8_t *)&rbuf[NBUF - 1][0];
+    {
+        const int32_t *lst = p.idxs + (int64_t)qi * p.K;
+        const int NI = (p.K + 63) / 64;
+        for (int i = wid; i < NI; i += NW) {
+            const int k = i * 64 + lane;
+            if (k < p.K) lds_dma4(lst + k, (LDS_AS int32_t *)&list[i * 64]);
+        }
+#pragma unroll
+        for (int j = wid; j < 16; j += NW) {
+            const int hh = hg * 16 + j < p.H ? hg * 16 + j : 0;  // heads beyond H: zeroed below
+            lds_dma16(p.q + ((int64_t)qi * p.H + hh) * D + lane * 8, (LDS_AS void *)(qlds + j * RS));
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // a3: qf[k] = q[h, 32k + 8g .. +7]
+    bf16x8_t qf[KS];
+    if (scorer) {
+        const LDS_AS uint8_t *Q = qlds + li * RS + g * 16;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) qf[k] = __builtin_bit_cast(bf16x8_t, *(const LDS_AS u32x4_t *)(Q + 64 * k));
+        if (h >= p.H) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) qf[k] = bf16x8_t{};
+        }
+    }
+
+    // Rounds 0 and 1 are requested from the raw list before the compaction
+    // (entries that are not rows are not fetched); afterwards only the rows
+    // whose number changed are requested again.  A later load into the same
+    // registers returns after the earlier one.
+    u32x4_t rg[2][RPW];
+    int spec[2][RPW];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) {
+            const int e = RR * r + RPW * wid + k;
+            const int v = __builtin_amdgcn_readfirstlane(e < p.K ? list[e] : -1);
+            spec[r][k] = v >= 0 && (int64_t)v < p.N ? v : -1;
+            if (spec[r][k] >= 0) load_row(spec[r][k], rg[r][k]);
+        }
+    // a1
+    const int n = compact_list<NT>((const LDS_AS int32_t *)&list[0], p.K, p.N, list, cnt);
+    const int nr = (n + RR - 1) / RR;
+    // the wave's rows of round r (lane k < RPW holds its k-th); positions
+    // past n repeat the round's first row, whose scores are masked
+    auto round_rows = [&](int r) {
+        const int e = RR * r + RPW * wid + (lane % RPW);
+        return list[e < n ? e : RR * r];
+    };
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (r < nr) {
+            const int rows = round_rows(r);
+#pragma unroll
+            for (int k = 0; k < RPW; ++k) {
+                const int rw = __builtin_amdgcn_readlane(rows, k);
+                if (rw != spec[r][k]) load_row(rw, rg[r][k]);
+            }
+        }
+    }
+
+    // Running reference and denominator of head h (the same in every wave),
+    // and O^T over this wave's columns: o[t][i] = O^T[CW wid + 16t + 4g + i, h].
+    float Rs = -INFINITY, lsum = 0.f;
+    f32x4_t o[NTL];
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // a4 / a5 (scorer wid): block wid of round r (in buffer Lb), published into pub[pbi]
+    auto score = [&](int r, const LDS_AS uint8_t *Lb, int pbi) {
+        const int cntb = n - RR * r - 16 * wid;  // valid rows of the block
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        const LDS_AS uint8_t *T = Lb + (16 * wid + li) * RS + g * 16;
+        constexpr int QKP = 4;  // K operands requested ahead
+        bf16x8_t ka[QKP];
+#pragma unroll
+        for (int k = 0; k < QKP; ++k) ka[k] = __builtin_bit_cast(bf16x8_t, *(const LDS_AS u32x4_t *)(T + 64 * k));
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k % QKP], qf[k], sacc, 0, 0, 0);
+            if (k + QKP < KS) ka[k % QKP] = __builtin_bit_cast(bf16x8_t, *(const LDS_AS u32x4_t *)(T + 64 * (k + QKP)));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // lane (li, g) holds rows 4g + i of head h
+        float sv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = 4 * g + i < cntb ? sacc[i] * p.qk_scale_log2 : -INFINITY;
+        const float lmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        float mb = Rs;
+        if (__ballot(lmax > Rs + MAX_SLACK)) {
+            float cmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
+            cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+            mb = cmax > Rs + MAX_SLACK ? cmax : Rs;
+        }
+        // the weights enter the value product as bf16; the sum counts the same rounded weights
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = sv[i] == -INFINITY ? 0.f : exp2_fast(sv[i] - mb);
+        const u32x2_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3])};
+        float ps = __uint_as_float(pw[0] << 16) + __uint_as_float(pw[0] & 0xffff0000u) +
+                   __uint_as_float(pw[1] << 16) + __uint_as_float(pw[1] & 0xffff0000u);
+        ps += shfl_xor_f(ps, 16);
+        ps += shfl_xor_f(ps, 32);
+        pub[pbi][wid][lane] = pw;
+        if (g == 0) {
+            mbs[pbi][wid][li] = mb;
+            lbs[pbi][wid][li] = ps;
+        }
+    };
+    // a6 (every wave): O^T[d, h] += V^T[d, j] P^T[j, h] over the round's blocks
+    // for d in this wave's columns.  A transpose load hands lane (li, g)
+    // column 16t + li of rows 4g .. 4g+3 of a block, the k-slice of the
+    // 16x16x16 MFMA whose B operand is the scorer's packed weights of those
+    // rows.  Every LDS read of the round is requested before any is used.
+    auto pv_round = [&](const LDS_AS uint8_t *Lb, int pbi) {
+        float mv[NB], lv[NB];
+        s16x4_t pbv[NB];
+        s16x4_t va[NB][NTL];
+        const LDS_AS uint8_t *V0 = Lb + (4 * g + (li >> 2)) * RS + (CW * wid + 4 * (li & 3)) * 2;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            mv[bb] = mbs[pbi][bb][li];
+            lv[bb] = lbs[pbi][bb][li];
+            pbv[bb] = __builtin_bit_cast(s16x4_t, pub[pbi][bb][lane]);
+#pragma unroll
+            for (int t = 0; t < NTL; ++t)
+                va[bb][t] = __builtin_bit_cast(s16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                            (LDS_AS bf16x4_t *)(V0 + 16 * bb * RS + 32 * t)));
+        }
+        float Rn = Rs;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) Rn = fmaxf(Rn, mv[bb]);
+        float c[NB];  // factor of each block against the new reference
+        bool scaled = false;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            c[bb] = lv[bb] == 0.f || mv[bb] == Rn ? 1.f : exp2_fast(mv[bb] - Rn);
+            scaled |= c[bb] != 1.f;
+        }
+        if (__ballot(Rn > Rs)) {  // a reference moved up (rare after the first round)
+            const float a = Rn > Rs ? (Rs == -INFINITY ? 0.f : exp2_fast(Rs - Rn)) : 1.f;
+            lsum *= a;
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) o[t] *= a;
+            Rs = Rn;
+        }
+        if (__ballot(scaled)) {
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+                for (int t = 0; t < NTL; ++t) {
+                    const f32x4_t z = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[bb][t], pbv[bb],
+                                                                               f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    o[t] += z * c[bb];
+                }
+                lsum += lv[bb] * c[bb];
+            }
+        } else {
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+                for (int t = 0; t < NTL; ++t)
+                    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[bb][t], pbv[bb], o[t], 0, 0, 0);
+                lsum += lv[bb];
+            }
+        }
+    };
+    // Iteration i: round i's rows into LDS buffer i % 3 and round i + 2's
+    // requested into the registers they leave; one barrier; the value
+    // product of round i - 1; the scoring of round i.  Buffer i % 3 was last
+    // read by iteration i - 2, and weight buffer i % 2 by iteration i - 1,
+    // both before the barrier of iteration i - 1 that every wave has passed.
+    auto iter = [&](int i, u32x4_t (&buf)[RPW], int pbi) {
+        LDS_AS uint8_t *Lw = (LDS_AS uint8_t *)&rbuf[i % NBUF][0];
+        if (i < nr) {
+            const int now = FP4 ? round_rows(i) : 0;
+#pragma unroll
+            for (int k = 0; k < RPW; ++k)
+                write_row(Lw, RPW * wid + k, FP4 ? __builtin_amdgcn_readlane(now, k) : 0, buf[k]);
+            if (i + 2 < nr) {
+                const int rows = round_rows(i + 2);
+#pragma unroll
+                for (int k = 0; k < RPW; ++k) load_row(__builtin_amdgcn_readlane(rows, k), buf[k]);
+            }
+            if constexpr (FP4) expand_fp4_own<D, RPW>(Lw, RS, p.rec2, list, RR * i, n, p.W);
+        }
+        __syncthreads();
+        if (i > 0) pv_round((const LDS_AS uint8_t *)&rbuf[(i - 1) % NBUF][0], pbi ^ 1);
+        if (i < nr && scorer) score(i, Lw, pbi);
+    };
+    // unrolled by two so that each round's register buffer is a fixed one
+    for (int i = 0; i <= nr; i += 2) {
+        iter(i, rg[0], 0);
+        if (i + 1 <= nr) iter(i + 1, rg[1], 1);
+    }
+
+    // a7 / a8: the sink joins the denominator (as in store_outputs); the
+    // outputs go straight to memory, 8 bytes per lane
+    float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if (p.sink != nullptr && h < p.H) {
+        const float zs = p.sink[h] * LOG2E;
+        const float Mx = fmaxf(Rs, zs);
+        const float alpha = Rs == -INFINITY ? 0.f : exp2_fast(Rs - Mx);
+        inv = Mx == -INFINITY ? 0.f : alpha / (lsum * alpha + exp2_fast(zs - Mx));
+    }
+    uint16_t *dst = p.out + ((int64_t)qi * p.H + h) * D;
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+        const int col = CW * wid + 16 * t + 4 * g;
+        float v0 = o[t][0] * inv, v1 = o[t][1] * inv, v2 = o[t][2] * inv, v3 = o[t][3] * inv;
+        if (col >= D - p.rd) {  // f3: rotary dims, pairs (col, col+1), (col+2, col+3)
+            const int64_t pr = (int64_t)(qi % p.T) * (p.rd / 2) + (col - (D - p.rd)) / 2;
+            rotate_back2(v0, v1, v2, v3, *(const float4 *)(p.rope + 2 * pr));
+        }
+        if (h < p.H) *(u32x2_t *)(dst + col) = u32x2_t{pack2_bf16(v0, v1), pack2_bf16(v2, v3)};
+    }
+}
+
 // a9: log-sum-exp merge of the splits.  Split s holds p_s (its output
 // normalised by its own denominator l_s; fp16 times the power of two x_s of
 // the row), its max m_s and l_s (log2 units).  With
@@ -1836,6 +2150,22 @@ WsLayout ws_layout(const sa_dims *d, int S) {
     return w;
 }
 
+// Unsplit launches at D = 512 whose (query, 16 heads) units all
+// fit the compute units at once, with lists of up to HS_MAX_K entries, run
+// the head-split kernel.  Measured on MI355X at 64 queries x 64 heads against
+// the deep-gather kernel with its planned splits: 11.3 / 12.7 / 15.7 / 17.1 /
+// 18.7 us against 13.4 / 16.1 / 18.7 / 21.4 / 22.5 us for lists of 128 / 192 /
+// 256 / 320 / 384 valid entries, even at 512 (23.4 against 23.8 us), behind
+// at 640 (27.6 against 25.1 us), where every row read by four head groups
+// costs more than the split partials save.
+constexpr int HS_MAX_K = 448;
+bool hs_fits(const sa_dims *d) {
+    if (d->D != 512 || d->K > HS_MAX_K) return false;
+    if (hs_static_lds(512) + list_lds_bytes(d->K) > (size_t)LDS_BYTES) return false;
+    const int cus = device_cu_count();
+    return cus > 0 && queries(d) * ((d->H + 15) / 16) <= cus;
+}
+
 // Split count for launches with fewer units than compute units.  A split
 // shortens every workgroup's share of the list, but its partials cost a
 // combine kernel worth about four 32-row chunks of the attention kernel plus
@@ -1847,6 +2177,7 @@ WsLayout ws_layout(const sa_dims *d, int S) {
 int plan_splits(const sa_dims *d) {
     const int cus = device_cu_count();
     if (cus < 0) return -SA_ERR_HIP;
+    if (hs_fits(d)) return 1;  // the head-split kernel needs no partials
     const int64_t units = queries(d) * head_groups(d->H);
     if (units <= 0 || units >= cus) return 1;
     int64_t smax = (cus + units - 1) / units;
@@ -2000,8 +2331,27 @@ bool use_mq(const FwdParams &p, int H) {
     return H > 16 && cus > 0 && (int64_t)p.units >= 2 * (int64_t)cus;
 }
 
+// One workgroup per (query, 16 heads); a query's head groups are consecutive
+// units, so they share an XCD (unit_of with bs a multiple of them).
+hipError_t launch_hs(FwdParams p, const sa_dims *d, hipStream_t stream) {
+    const size_t lb = list_lds_bytes(p.K);
+    p.HG = (d->H + 15) / 16;
+    const int64_t units = queries(d) * p.HG;
+    p.units = (int32_t)units;
+    const int64_t even = (units + 7) / 8;
+    const int64_t bs = ((even + p.HG - 1) / p.HG) * p.HG;
+    p.bs = (int32_t)bs;
+    p.per_xcd = (int32_t)bs;
+    if (p.rec2 > 0)
+        hipLaunchKernelGGL((attn_fwd_hs_kernel<512, true>), dim3(8 * p.per_xcd), dim3(512), lb, stream, p);
+    else
+        hipLaunchKernelGGL((attn_fwd_hs_kernel<512, false>), dim3(8 * p.per_xcd), dim3(512), lb, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t run_fwd(const FwdParams &p, const sa_dims *d, hipStream_t stream) {
     const int D = d->D, H = d->H;
+    if (p.S == 1 && hs_fits(d)) return launch_hs(p, d, stream);
     if (use_mq(p, H)) {
         const bool two = H > 32;
         switch (D) {
@@ -2252,6 +2602,7 @@ const char *sparse_attn_plan_kernel(const sa_dims *d, int32_t num_splits) {
         S = plan_splits(d);
         if (S < 0) return nullptr;
     }
+    if (S == 1 && hs_fits(d)) return "attn_fwd_hs_kernel<512,false>";
     FwdParams p{};
     p.units = (int32_t)(queries(d) * head_groups(d, S) * S);
     if (use_mq(p, d->H)) {

@@ -301,7 +301,8 @@ def test_sixty_four_head_workgroups(ref, S):
 @pytest.mark.parametrize("B,T,K,expected", [
     (64, 1, 640, 4),     # decode
     (32, 1, 640, 4),     # long context
-    (64, 1, 128, 1),     # sliding window only
+    (64, 1, 128, 1),     # sliding window only (head split)
+    (64, 1, 384, 1),     # short decode lists (head split)
     (256, 1, 640, 1),    # ragged batch
     (1, 4096, 640, 1),   # prefill
     (1, 1, 640, 4),      # a single query: more splits cost more in the combine
@@ -332,6 +333,99 @@ def test_many_query_splits_stress_and_long_lists(ref):
     # the longest supported list (2048 entries, compacted in place), mostly unused
     wl2 = wl.make_random(211, 1, 2 * T, 64, 512, 2100, 2048, p_unused=0.97)
     check(ref, wl2, 0, what="many-query K=2048")
+
+
+# ------------------------------------------------- head-split path (one split, short lists)
+# Unsplit launches at D=512 with K <= 448 whose (query, 16 heads) units all fit
+# the compute units at once run the head-split kernel; every case here is
+# such a launch (a few queries), checked against the oracle.
+
+HS = "attn_fwd_hs_kernel<512,false>"
+
+
+def plan_name(B, T, H, D, K, S, N=8320):
+    import ctypes
+    from sparse_top_latent_amd import _lib
+    d = _lib.SaDims(B, T, H, D, N, K)
+    return _lib.lib().sparse_attn_plan_kernel(ctypes.byref(d), S).decode()
+
+
+def test_head_split_dispatch():
+    import ctypes
+    torch = torch_mod()
+    from sparse_top_latent_amd import _lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert plan_name(4, 1, 64, 512, 128, 0) == HS
+    assert plan_name(4, 1, 64, 512, 448, 1) == HS
+    assert plan_name(4, 1, 64, 512, 449, 1) != HS      # longer lists: deep-gather kernel
+    assert plan_name(4, 1, 64, 512, 128, 2) != HS      # explicit splits
+    assert plan_name(4, 1, 64, 256, 128, 0) != HS      # D = 256
+    assert plan_name(cus // 4, 1, 64, 512, 128, 1) == HS
+    assert plan_name(cus // 4 + 1, 1, 64, 512, 128, 1) != HS   # 4 units per query overflow
+    assert plan_name(3, 2, 40, 512, 200, 0) == HS      # 3 head groups, the last one partial
+    d = _lib.SaDims(4, 1, 64, 512, 8320, 384)
+    assert _lib.lib().sparse_attn_plan_splits(ctypes.byref(d)) == 1
+
+
+@pytest.mark.parametrize("K", [1, 16, 47, 48, 49, 96, 143, 144, 145, 200, 448])
+def test_head_split_round_boundaries(ref, K):
+    # lists around one 48-entry round and three rounds (the LDS buffers' reuse)
+    w = wl.make_random(400 + K, 2, 2, 64, 512, 500, K, p_unused=0.0)
+    assert plan_name(2, 2, 64, 512, K, 1, N=500) == HS
+    check(ref, w, 1, what=f"head split K={K}")
+
+
+def test_head_split_partial_head_group_unused_and_repeats(ref):
+    # H=40: the last head group holds 8 heads beyond H; ~30% unused entries,
+    # repeats, and entries beyond N skipped; planned and explicit one split
+    w = wl.make_random(410, 3, 2, 40, 512, 300, 200, p_unused=0.3, allow_repeats=True)
+    bad = w.idxs.copy()
+    bad[0, 0, 3] = w.N
+    bad[2, 1, 100] = w.N + 7
+    clean = np.where(bad >= w.N, -1, bad).astype(np.int32)
+    got = run_gpu(w, 0, bad)
+    assert_close(got, ref(w.q, w.kv_host(), w.sink, clean, w.scale), "head split H=40")
+    check(ref, w, 1, sink=None, what="head split H=40 no sink")
+
+
+def test_head_split_rising_scores(ref):
+    # every list holds all 400 rows in ascending order; row r has r/400 in
+    # dim 0 and every q has 315 there, so the scores rise by ~20 log2 units
+    # along the list (the rest of each score stays ~N(0, 1)): each head's max
+    # keeps rising from round to round and within rounds, the reference moves
+    # and blocks go through the scaled path, while the outputs stay O(1)
+    import copy
+    w = copy.deepcopy(wl.make_random(411, 2, 2, 64, 512, 400, 400, p_unused=0.0))
+    w.idxs = np.sort(w.idxs, axis=-1).astype(np.int32)
+    for b in range(w.B):
+        w.vals[b] = w.vals[b].copy()
+        w.vals[b][:, 0] = wl.to_bf16_bits((w.rows[b] / 400.0).astype(np.float32))
+    q = w.q.copy()
+    q[..., 0] = wl.to_bf16_bits(np.float32(315.0))
+    check(ref, w, 1, q_bits=q, what="head split rising scores")
+    check(ref, w, 0, q_bits=q, sink=np.full(64, 25.0), what="head split rising scores, sink 25")
+    check(ref, w, 3, q_bits=q, what="deep gather S=3, rising scores")
+
+
+def test_head_split_fp4_rows_decode_batch():
+    # 64 queries, 128-entry window + 256 compressed entries, FP4 compressed
+    # rows: bit for bit the bf16 two-source result, both on the head split
+    torch = torch_mod()
+    w = wl.make_random(412, 64, 1, 64, 512, 640, 384, p_unused=0.1)
+    if torch.cuda.get_device_properties(0).multi_processor_count >= 256:
+        assert plan_name(64, 1, 64, 512, 384, 0, N=640) == HS
+    check_fp4(w, 128, 0, "head split fp4 64 queries")
+
+
+def test_head_split_deterministic_and_close_to_deep_gather(ref):
+    w = wl.make_random(413, 4, 2, 64, 512, 600, 300, p_unused=0.2)
+    runs = [run_gpu(w, 1) for _ in range(3)]
+    assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
+    split = run_gpu(w, 3)   # the deep-gather kernel with partials
+    exp = ref(w.q, w.kv_host(), w.sink, w.idxs, w.scale)
+    assert_close(runs[0], exp, "head split")
+    assert_close(split, exp, "deep gather S=3")
+    assert np.abs(runs[0] - split).max() <= 2 * MAX_ABS
 
 
 # ------------------------------------------------- two-source rows (window + compressed)
