@@ -62,6 +62,10 @@ def parse():
                     help="run plain 256 MiB copies first (HBM counter calibration)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="time only the headline workload (profiling runs)")
+    ap.add_argument("--list-sweep", action="store_true",
+                    help="also time decode batches (64 queries, 64 heads) with lists of "
+                         "128..640 entries: the planned kernel against the deep-gather "
+                         "kernel at its best of 2-4 splits")
     return ap.parse_args()
 
 
@@ -445,6 +449,36 @@ def main():
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
         line["workloads"] = res
+
+    if args.list_sweep:
+        # where the head-split kernel takes over: K-entry lists (all valid), and
+        # 640-entry lists with about 160 or 320 valid entries
+        sweep = []
+        cases = [(K, 0.0) for K in (128, 192, 256, 320, 384, 448, 512, 640)]
+        cases += [(640, 1 - 160 / 640), (640, 1 - 320 / 640)]
+        keep = args.splits
+        for K, pu in cases:
+            ws_ = wl.make_random(11, 64, 1, 64, 512, 8320, K, p_unused=pu, scale=512 ** -0.5)
+            args.splits = 0
+            fp, sp = measure(ws_, R, warm_cache=False)
+            best = None
+            for S_ in (2, 3, 4):
+                args.splits = S_
+                fs, ss = measure(ws_, R, warm_cache=False)
+                if best is None or fs["ms_per_step"] < best[1]:
+                    best = (S_, fs["ms_per_step"])
+                del ss
+            sweep.append({"K": K, "valid_entries": fp["config"]["valid_entries"],
+                          "planned": {"kernel": fp["roofline"]["kernel"],
+                                      "splits": fp["config"]["splits"],
+                                      "us_per_step": round(fp["ms_per_step"] * 1e3, 2)},
+                          "deep_gather_best": {"splits": best[0],
+                                               "us_per_step": round(best[1] * 1e3, 2)}})
+            del sp
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        args.splits = keep
+        line["list_sweep"] = sweep
 
     if not args.no_cpu_baseline:
         import ctypes

@@ -375,6 +375,15 @@ def test_head_split_round_boundaries(ref, K):
     check(ref, w, 1, what=f"head split K={K}")
 
 
+@pytest.mark.parametrize("H", [8, 16, 17, 33])
+def test_head_split_head_counts(ref, H):
+    # a head tile half empty (8), exactly one (16), one head over a tile (17:
+    # a second group with 15 heads beyond H), three groups (33)
+    w = wl.make_random(420 + H, 2, 3, H, 512, 260, 150, p_unused=0.2)
+    assert plan_name(2, 3, H, 512, 150, 0, N=260) == HS
+    check(ref, w, 0, what=f"head split H={H}")
+
+
 def test_head_split_partial_head_group_unused_and_repeats(ref):
     # H=40: the last head group holds 8 heads beyond H; ~30% unused entries,
     # repeats, and entries beyond N skipped; planned and explicit one split
