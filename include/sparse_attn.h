@@ -175,8 +175,13 @@ int32_t sparse_attn_fp4_record_bytes(int32_t D);
  * bytes D/2 .. D/2 + D/16 - 1 are OCP E4M3 scales (scale g for elements
  * 16g .. 16g+15), the rest is padding.  Element i of the row is
  * E2M1(code i) x E4M3(scale i/16); the product is exact in bf16, and the result
- * equals sparse_attn_fwd_2src on those bf16 rows, bit for bit.  The window rows
- * stay bf16.  A NaN scale code makes its group NaN. */
+ * equals sparse_attn_fwd_2src on those bf16 rows, bit for bit (the same kernel
+ * runs for both).  The window rows stay bf16.  A NaN scale code makes its
+ * group NaN.  On the head-split kernel (see sparse_attn_fwd) each record is
+ * expanded in LDS before the round's barrier, which costs more than in the
+ * deep-gather kernel: measured at 64 queries x 64 heads with 128 window + 256
+ * compressed entries, 26.8 us against 23.0 us with num_splits = 3 (the
+ * deep-gather kernel; bf16 rows 16.9 and 20.6 us). */
 int sparse_attn_fwd_2src_fp4(const void *q, const void *kv_win, int32_t win_rows,
                              const void *cmp_records, int32_t cmp_rows, int32_t W,
                              const float *sink, const int32_t *idxs, float scale, void *out,
