@@ -4,22 +4,27 @@
 // excerpt (o = sparse_attn(q, kv, attn_sink, topk_idxs, softmax_scale)); the
 // semantics and layouts are stated in include/sparse_attn.h.
 //
-// Kernels
-//   attn_fwd    one workgroup per (query, head group, split).  Steps:
-//               index decode + compaction of the query's list into LDS, a
-//               per-split slice of the valid entries, then chunks of 32 rows:
-//               LDS-DMA gather of the rows (16 B per lane, a 4-chunk ring),
-//               S^T = K Q^T on 16x16x32 bf16 MFMAs, the online sink-softmax in
-//               float32, O^T += V^T P^T on MFMAs with V read through LDS
-//               transpose loads.  Epilogue: bf16 output, or a split's fp16
-//               partial (power-of-two scaled per half row), staged through
-//               LDS into whole-row stores.
-//   combine     log-sum-exp merge of split partials plus the sink -> bf16.
-//   check_idxs  counts entries >= N.
-//
-// Work split inside a workgroup: a pair of waves owns 16 heads (one wave per
-// half of the head dimension); all waves share one LDS copy of each row chunk
-// (one HBM read per row per workgroup).
+// Kernels (the host picks one attention kernel per call from the dims)
+//   attn_fwd_kernel     deep gather: one workgroup per (query, 64 or 32 heads,
+//                       split).  Index decode + compaction of the query's list
+//                       into LDS, a per-split slice of the valid entries, then
+//                       chunks of 32 rows: LDS-DMA gather into a 4-chunk ring,
+//                       S^T = K Q^T on 16x16x32 bf16 MFMAs (a pair of waves per
+//                       16 heads, one per half of d), the online sink softmax in
+//                       float32, O^T += V^T P^T with V through LDS transpose
+//                       loads.  Epilogue: bf16 output, or a split's fp16
+//                       partial (a power of two per row), staged through LDS
+//                       into whole-row stores.
+//   attn_fwd_mq_kernel  many queries (prefill): the same steps with two
+//                       workgroups of four waves per compute unit, each wave
+//                       over the whole of d for its 16 heads.
+//   attn_fwd_hs_kernel  head split (short lists, unsplit): one workgroup per
+//                       (query, 16 heads) over the whole list; rows staged
+//                       through registers, no partials.
+//   combine_kernel      log-sum-exp merge of split partials plus the sink.
+//   topk_reg_kernel /   the lists' compressed segment: radix select of the k
+//   topk_long_kernel    best scores per row, in index order.
+//   check_idxs_kernel   counts entries >= N (checked mode).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
