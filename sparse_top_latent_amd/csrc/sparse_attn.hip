@@ -1354,10 +1354,12 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 // ones the bf16 build reads, so both builds agree bit for bit.
 //
 // The list is consumed in rounds of RR = 48 entries.  Rows travel through
-// registers: each of the 8 waves loads RPW = 6 rows of round i + 2 (ordinary
-// 16-byte loads, the compiler tracks them) while round i is computed, and
-// writes round i into one of three LDS round buffers, so no LDS holds rows in
-// flight.  Iteration i: round i's rows go to LDS, one barrier, then
+// registers: each of the 8 waves requests RPW = 6 rows of round i + 2
+// (ordinary 16-byte loads, the compiler tracks them) while round i is
+// computed, and writes round i into one of three LDS round buffers, so no LDS
+// holds rows in flight.  (The compiler's waits before those writes cover every
+// load in flight, round i + 1's too; a variant with a fixed count of loads per
+// round, which let it wait for round i alone, measured no faster.)  Iteration i: round i's rows go to LDS, one barrier, then
 //   - waves 0..2 (the scorers) each take one 16-row block of round i: S^T over
 //     all of d (q of the 16 heads in registers), the block's softmax weights
 //     as bf16, published with the block's reference max and weight sum;
