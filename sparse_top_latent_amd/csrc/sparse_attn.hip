@@ -166,6 +166,26 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// Sum and max of x over the lanes l mod 16 + 16k, k = 0..3 (the four 16-lane
+// rows of a wave), returned in every lane: two lane swaps on the VALU
+// (gfx950's v_permlane16_swap and v_permlane32_swap) in place of two LDS
+// permutes.  Swapping x with itself returns, in its two results, x of the
+// lane and x of the lane one row (then one half-wave) away, in the same order
+// in every lane, so all lanes agree bit for bit, as with xor shuffles.  Every
+// lane of the wave must be active.
+__device__ __forceinline__ float sum_rows4(float x) {
+    const u32x2_t p = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false));
+    const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const u32x2_t q = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false));
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float max_rows4(float x) {
+    const u32x2_t p = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false));
+    const float y = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const u32x2_t q = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false));
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -424,8 +444,7 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
             for (int u = 0; u < NU; ++u)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[t][u][i]));
-            amax = fmaxf(amax, shfl_xor_f(amax, 16));
-            amax = fmaxf(amax, shfl_xor_f(amax, 32));
+            amax = max_rows4(amax);
             if (g == 0) red[wid * HWG + 16 * t + li] = amax;
         }
         __syncthreads();
@@ -980,8 +999,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
                                fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
             float alpha = 1.f;
             if (__ballot(lmax > m[t] + MAX_SLACK)) {
-                float cmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
-                cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+                const float cmax = max_rows4(lmax);
                 const bool raise = cmax > m[t] + MAX_SLACK;
                 const float mnew = raise ? cmax : m[t];
                 alpha = exp2_fast(m[t] - mnew);
@@ -1017,8 +1035,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     LDS_AS float *red = lh + HWG;
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
-        float ltot = lsum[t] + shfl_xor_f(lsum[t], 16);
-        ltot += shfl_xor_f(ltot, 32);
+        const float ltot = sum_rows4(lsum[t]);
         if (dh == 0 && g == 0) {
             mh[hq * HW + 16 * t + li] = m[t];
             lh[hq * HW + 16 * t + li] = ltot;
@@ -1251,8 +1268,7 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
                                  fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
         float alpha = 1.f;
         if (__ballot(lmax > m + MAX_SLACK)) {
-            float cmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
-            cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+            const float cmax = max_rows4(lmax);
             const float mnew = cmax > m + MAX_SLACK ? cmax : m;
             alpha = exp2_fast(m - mnew);
             lsum *= alpha;
@@ -1328,8 +1344,7 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     LDS_AS float *lh = mh + HWG;
     LDS_AS float *red = lh + HWG;
     static_assert(sizeof(xp) >= (2 + NW) * HWG * sizeof(float), "epilogue state fits in xp");
-    float ltot = lsum + shfl_xor_f(lsum, 16);
-    ltot += shfl_xor_f(ltot, 32);
+    const float ltot = sum_rows4(lsum);
     if (g == 0) {
         mh[16 * wid + li] = m;
         lh[16 * wid + li] = ltot;
@@ -1520,8 +1535,7 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
         const float lmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
         float mb = Rs;
         if (__ballot(lmax > Rs + MAX_SLACK)) {
-            float cmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
-            cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+            const float cmax = max_rows4(lmax);
             mb = cmax > Rs + MAX_SLACK ? cmax : Rs;
         }
         // the weights enter the value product as bf16; the sum counts the same rounded weights
@@ -1531,8 +1545,7 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
         const u32x2_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3])};
         float ps = __uint_as_float(pw[0] << 16) + __uint_as_float(pw[0] & 0xffff0000u) +
                    __uint_as_float(pw[1] << 16) + __uint_as_float(pw[1] & 0xffff0000u);
-        ps += shfl_xor_f(ps, 16);
-        ps += shfl_xor_f(ps, 32);
+        ps = sum_rows4(ps);
         pub[pbi][wid][lane] = pw;
         if (g == 0) {
             mbs[pbi][wid][li] = mb;
