@@ -1674,7 +1674,7 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
 // a small LDS table (one per row).  Workgroups are laid out so that the rows
 // of a query are merged on the XCD whose workgroups wrote its partials (the
 // same blockIdx-to-XCD order as attn_fwd), where they may still sit in L2.
-template <int D>
+template <int D, int SB>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ ws_o,
                                                       const float *__restrict__ ws_m,
                                                       const float *__restrict__ ws_l,
@@ -1688,7 +1688,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     constexpr int LPR = D / 8;       // lanes per row
     constexpr int RPW = 64 / LPR;    // rows per wave
     constexpr int RWG = 4 * RPW;     // rows per workgroup
-    constexpr int SB = 8;            // splits per batch of row loads
+    // SB: splits per batch of row loads (4 for launches with up to 4 splits, else 8)
     constexpr int SPL = MAX_SPLITS / LPR > 0 ? MAX_SPLITS / LPR : 1;  // scalar slots per lane
     __shared__ float coef[RWG][MAX_SPLITS];
 
@@ -1705,9 +1705,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     const int h = ok ? (int)(qh % H) : 0;
     const int c8 = sl * 8;
     const int64_t slot0 = qi * S * H + h;    // slot of split j: slot0 + j * H
-    // a10: the splits this query's list was cut into (the first Sq slots)
-    int Sq = ok ? ws_plan[qi] : 1;
-    Sq = Sq < 1 ? 1 : (Sq > S ? S : Sq);
+    // a10: the splits this query's list was cut into (the first Sq slots).
+    // The first batch of partials and every scalar are requested before Sq
+    // arrives (all S slots lie inside the workspace; a slot the plan leaves
+    // out may hold stale bits and is masked once Sq is known), so the merge
+    // costs one memory round trip, not two.
+    // Lanes past the last row (!ok) read row 0's slots, which exist, and
+    // store nothing: every load below is unconditional in the lane, so none
+    // sits in a branch of its own and the compiler issues them all before
+    // waiting for any.
+    int Sq = ws_plan[qi];
 
     // The partials are read once: non-temporal loads with up to four splits
     // (measured faster there; with eight, ordinary loads were faster).
@@ -1715,29 +1722,45 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         const u32x4_t *ptr = (const u32x4_t *)(ws_o + (slot0 + (int64_t)j * H) * D + c8);
         return S <= 4 ? __builtin_nontemporal_load(ptr) : *ptr;
     };
+    // the first batch: slots past S read slot S - 1 again (no branch per
+    // load) and are zeroed below with the ones past Sq
     u32x4_t v[SB];
 #pragma unroll
-    for (int j = 0; j < SB; ++j) v[j] = ok && j < Sq ? part(j) : u32x4_t{0, 0, 0, 0};
-    // rotary dims: the (cos, sin) of the lane's four pairs
-    const bool rot = ok && c8 >= D - rd;
+    for (int j = 0; j < SB; ++j) v[j] = part(j < S ? j : S - 1);
+    // rotary dims: the (cos, sin) of the lane's four pairs (other lanes read
+    // the first pair's and keep the identity)
+    const bool rot = c8 >= D - rd;
     float4 cs0 = {1.f, 0.f, 1.f, 0.f}, cs1 = cs0;
-    if (rot) {
-        const float *f = rope + 2 * ((int64_t)(qi % T) * (rd / 2) + (c8 - (D - rd)) / 2);
-        cs0 = *(const float4 *)f;
-        cs1 = *(const float4 *)(f + 4);
+    if (rd > 0) {
+        const float *f = rope + 2 * ((int64_t)(qi % T) * (rd / 2) + (rot ? (c8 - (D - rd)) / 2 : 0));
+        const float4 r0 = *(const float4 *)f, r1 = *(const float4 *)(f + 4);
+        if (rot) cs0 = r0, cs1 = r1;
     }
-    // lane sl holds the scalars of splits sl, sl + LPR, ...
+    // lane sl holds the scalars of splits sl, sl + LPR, ... (lanes past S
+    // read split 0's and drop them)
     float mj[SPL], lj[SPL], xj[SPL];
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
         const int j = sl + k * LPR;
-        const bool has = ok && j < Sq;
-        const int64_t slot = slot0 + (int64_t)j * H;
-        mj[k] = has ? ws_m[slot] : -INFINITY;
-        lj[k] = has ? ws_l[slot] : 0.f;
-        xj[k] = has ? ws_x[slot] : 0.f;
+        const int64_t slot = slot0 + (int64_t)(j < S ? j : 0) * H;
+        mj[k] = ws_m[slot];
+        lj[k] = ws_l[slot];
+        xj[k] = ws_x[slot];
     }
-    const float mz = ok && sink != nullptr ? sink[h] * LOG2E : -INFINITY;
+    const float zs = sink != nullptr ? sink[h] : 0.f;
+    Sq = Sq < 1 ? 1 : (Sq > S ? S : Sq);
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+        if (!ok || sl + k * LPR >= Sq) {
+            mj[k] = -INFINITY;
+            lj[k] = 0.f;
+            xj[k] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+        if (!ok || j >= Sq) v[j] = u32x4_t{0, 0, 0, 0};
+    const float mz = ok && sink != nullptr ? zs * LOG2E : -INFINITY;
     float mx = mz;
 #pragma unroll
     for (int k = 0; k < SPL; ++k) mx = fmaxf(mx, mj[k]);
@@ -2254,11 +2277,15 @@ hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
     const float *wx = (const float *)((const uint8_t *)ws + L.x_off);
     const int32_t *wp = (const int32_t *)((const uint8_t *)ws + L.plan_off);
     uint16_t *o = (uint16_t *)out;
+#define SA_COMBINE(DD, SB) \
+    hipLaunchKernelGGL((combine_kernel<DD, SB>), dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T)
+    const bool small = S <= 4;  // one batch of four holds every split
     switch (d->D) {
-        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
-        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
-        default: hipLaunchKernelGGL(combine_kernel<512>, dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T); break;
+        case 128: if (small) SA_COMBINE(128, 4); else SA_COMBINE(128, 8); break;
+        case 256: if (small) SA_COMBINE(256, 4); else SA_COMBINE(256, 8); break;
+        default: if (small) SA_COMBINE(512, 4); else SA_COMBINE(512, 8); break;
     }
+#undef SA_COMBINE
     return hipGetLastError();
 }
 
