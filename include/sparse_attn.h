@@ -95,7 +95,7 @@ size_t sparse_attn_workspace_bytes_splits(const sa_dims *d, int32_t num_splits);
 
 /* The whole step: out = sparse_attn(q, kv, sink, idxs, scale), the call of the
  * pages' Attention.forward excerpt with the dims and a workspace made explicit.
- * An unsplit launch at D = 512 with K <= 448 whose B*T*ceil(H/16) units all fit
+ * An unsplit launch at D = 512 with K <= 512 whose B*T*ceil(H/16) units all fit
  * the device's compute units at once runs the head-split kernel: one workgroup
  * per query and 16 heads over the whole list, no workspace; the planner then
  * picks one split.  Its softmax weights are rounded to bf16 against a

@@ -2195,13 +2195,13 @@ WsLayout ws_layout(const sa_dims *d, int S) {
 
 // Unsplit launches at D = 512 whose (query, 16 heads) units all
 // fit the compute units at once, with lists of up to HS_MAX_K entries, run
-// the head-split kernel.  Measured on MI355X at 64 queries x 64 heads against
-// the deep-gather kernel with its planned splits: 11.3 / 12.7 / 15.7 / 17.1 /
-// 18.7 us against 13.4 / 16.1 / 18.7 / 21.4 / 22.5 us for lists of 128 / 192 /
-// 256 / 320 / 384 valid entries, even at 512 (23.4 against 23.8 us), behind
-// at 640 (27.6 against 25.1 us), where every row read by four head groups
-// costs more than the split partials save.
-constexpr int HS_MAX_K = 448;
+// the head-split kernel.  Measured on MI355X at 64 queries x 64 heads, all
+// entries valid, against the deep-gather kernel's best of 2 to 4 splits:
+// 11.4 / 13.0 / 15.8 / 17.3 / 18.9 / 21.8 / 23.3 us against 15.9 / 17.3 / 18.5
+// / 20.0 / 21.2 / 22.3 / 23.4 us for lists of 128 / 192 / 256 / 320 / 384 /
+// 448 / 512 entries, behind at 640 (27.9 against 24.7 us), where every row
+// read by four head groups costs more than the split partials save.
+constexpr int HS_MAX_K = 512;
 bool hs_fits(const sa_dims *d) {
     if (d->D != 512 || d->K > HS_MAX_K) return false;
     if (hs_static_lds(512) + list_lds_bytes(d->K) > (size_t)LDS_BYTES) return false;

@@ -303,6 +303,7 @@ def test_sixty_four_head_workgroups(ref, S):
     (32, 1, 640, 4),     # long context
     (64, 1, 128, 1),     # sliding window only (head split)
     (64, 1, 384, 1),     # short decode lists (head split)
+    (64, 1, 512, 1),     # the longest lists the head split takes
     (256, 1, 640, 1),    # ragged batch
     (1, 4096, 640, 1),   # prefill
     (1, 1, 640, 4),      # a single query: more splits cost more in the combine
@@ -336,7 +337,7 @@ def test_many_query_splits_stress_and_long_lists(ref):
 
 
 # ------------------------------------------------- head-split path (one split, short lists)
-# Unsplit launches at D=512 with K <= 448 whose (query, 16 heads) units all fit
+# Unsplit launches at D=512 with K <= 512 whose (query, 16 heads) units all fit
 # the compute units at once run the head-split kernel; every case here is
 # such a launch (a few queries), checked against the oracle.
 
@@ -356,8 +357,8 @@ def test_head_split_dispatch():
     from sparse_top_latent_amd import _lib
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert plan_name(4, 1, 64, 512, 128, 0) == HS
-    assert plan_name(4, 1, 64, 512, 448, 1) == HS
-    assert plan_name(4, 1, 64, 512, 449, 1) != HS      # longer lists: deep-gather kernel
+    assert plan_name(4, 1, 64, 512, 512, 1) == HS
+    assert plan_name(4, 1, 64, 512, 513, 1) != HS      # longer lists: deep-gather kernel
     assert plan_name(4, 1, 64, 512, 128, 2) != HS      # explicit splits
     assert plan_name(4, 1, 64, 256, 128, 0) != HS      # D = 256
     assert plan_name(cus // 4, 1, 64, 512, 128, 1) == HS
@@ -367,11 +368,11 @@ def test_head_split_dispatch():
     assert _lib.lib().sparse_attn_plan_splits(ctypes.byref(d)) == 1
 
 
-@pytest.mark.parametrize("K", [1, 16, 47, 48, 49, 96, 143, 144, 145, 200, 448])
+@pytest.mark.parametrize("K", [1, 16, 47, 48, 49, 96, 143, 144, 145, 200, 448, 512])
 def test_head_split_round_boundaries(ref, K):
     # lists around one 48-entry round and three rounds (the LDS buffers' reuse)
-    w = wl.make_random(400 + K, 2, 2, 64, 512, 500, K, p_unused=0.0)
-    assert plan_name(2, 2, 64, 512, K, 1, N=500) == HS
+    w = wl.make_random(400 + K, 2, 2, 64, 512, 600, K, p_unused=0.0)
+    assert plan_name(2, 2, 64, 512, K, 1, N=600) == HS
     check(ref, w, 1, what=f"head split K={K}")
 
 
