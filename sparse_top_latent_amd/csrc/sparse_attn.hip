@@ -121,17 +121,18 @@ __device__ __forceinline__ void rotate_back2(float &x0, float &y0, float &x1, fl
     x0 = a0, y0 = b0, x1 = a1, y1 = b1;
 }
 
-// Row swizzle of the 16-byte chunks of a 16-bit row in an LDS staging area
-// (the epilogue's output rows): chunk c of row r lives at position
-// c ^ swz<CPR>(r).  gfx950's LDS serves a b128 access 32 lanes (512 bytes)
-// per pass, so the 32 lanes of a half-wave must land in 32 distinct 16-byte
-// bank slots (slot = byte address / 16 mod 32).  Rows of 1 KB or 512 B all
-// start on slot 0, so swz = 2r mod 32; 256-byte rows alternate between slot
-// 0 and 16, so the rows of one parity share 2*(r/2) mod 16.
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-    return CPR >= 32 ? (2 * r) & 31 : (2 * (r >> 1)) & 15;
-}
+// Swizzle of the epilogue's output staging rows (16-bit rows of 256 B to
+// 1 KB in LDS): 8-byte piece k of row r lives at piece position k ^ (r & 15).
+// A staging write stores one 8-byte piece per lane, the 16 lanes of a lane
+// group on 16 rows at the same piece; gfx950's LDS takes such a b64 write 16
+// lanes (128 bytes, 32 four-byte banks) per cycle, so the 16 pieces must land
+// on 16 distinct 8-byte bank pairs ((byte address / 8) mod 16), which the
+// row-dependent XOR gives (every row starts on pair 0).  Measured with
+// SQ_LDS_BANK_CONFLICT: 12 conflict cycles per write instruction with a
+// 16-byte-granular swizzle of 2r, 4 with r, none with this one.  Reading a
+// 16-byte slot back gives one 16-byte chunk of the row, its two halves
+// swapped when r is odd (see store_outputs).
+__device__ __forceinline__ int stage_swz(int r) { return r & 15; }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -380,9 +381,9 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 // denominator, then staged through LDS (HWG rows of 2D bytes at `stage_out`,
 // which the caller has freed with a barrier) so that each wave instruction
 // stores whole rows: the final output as bf16, a split's partial as fp16
-// divided by a power of two per row.  In LDS, 16-byte chunk c of head row hl
-// sits at position c ^ swz(hl), which keeps the 16 rows written by one store
-// instruction on distinct banks.
+// divided by a power of two per row.  In LDS, 8-byte piece k (columns 4k ..
+// 4k + 3) of head row hl sits at piece position k ^ stage_swz(hl), which keeps
+// the 16 rows written by one store instruction on distinct banks.
 template <int D, int NW, int NTL>
 __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t (&o)[NTL][D / NW / 16],
                                               const LDS_AS float *mh, const LDS_AS float *lh,
@@ -419,8 +420,8 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
             LDS_AS uint8_t *Rrow = stage_out + hl * (D * 2);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                const int col = wid * DW + 16 * u + 4 * g;  // first of 4 columns
-                const int pos = (col >> 3) ^ swz<C16>(hl);
+                const int col = wid * DW + 16 * u + 4 * g;  // first of 4 columns (piece col / 4)
+                const int pk = (col >> 2) ^ stage_swz(hl);
                 float v0 = o[t][u][0] * inv[t], v1 = o[t][u][1] * inv[t];
                 float v2 = o[t][u][2] * inv[t], v3 = o[t][u][3] * inv[t];
                 if (col >= D - p.rd) {  // rotary dims: pairs (col, col+1), (col+2, col+3)
@@ -428,7 +429,7 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
                     rotate_back2(v0, v1, v2, v3, *(const float4 *)(p.rope + 2 * pr));
                 }
                 const u32x2_t w = {pack2_bf16(v0, v1), pack2_bf16(v2, v3)};
-                *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
+                *(LDS_AS u32x2_t *)(Rrow + pk * 8) = w;
             }
         }
     } else {
@@ -464,10 +465,10 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 const int col = wid * DW + 16 * u + 4 * g;
-                const int pos = (col >> 3) ^ swz<C16>(hl);
+                const int pk = (col >> 2) ^ stage_swz(hl);
                 const u32x2_t w = {pack2_f16(o[t][u][0] * down, o[t][u][1] * down),
                                    pack2_f16(o[t][u][2] * down, o[t][u][3] * down)};
-                *(LDS_AS u32x2_t *)(Rrow + pos * 16 + (col & 7) * 2) = w;
+                *(LDS_AS u32x2_t *)(Rrow + pk * 8) = w;
             }
             if (wid == 0 && g == 0 && h < p.H) {
                 const int64_t slot = ((int64_t)qi * p.S + s) * p.H + h;
@@ -496,8 +497,13 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
     for (int it = 0; it < NIT; ++it) {
         const int i = it * NT + tid;
         const int r = i / C16, pos = i % C16;
+        // slot pos holds pieces 2 pos and 2 pos + 1, i.e. pieces (2 pos) ^ z and
+        // (2 pos + 1) ^ z of the row (z = stage_swz(r)): chunk pos ^ (z >> 1),
+        // its halves swapped when z is odd
+        const int z = stage_swz(r);
+        const u32x4_t val = (z & 1) ? u32x4_t{v[it][2], v[it][3], v[it][0], v[it][1]} : v[it];
         if (hbase + r < p.H)
-            __builtin_nontemporal_store(v[it], (u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ swz<C16>(r)) << 3)));
+            __builtin_nontemporal_store(val, (u32x4_t *)(dst + (int64_t)(hbase + r) * D + ((pos ^ (z >> 1)) << 3)));
     }
 }
 
