@@ -986,8 +986,12 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         // of head tile t.  The kept max m only moves when a score beats it by
         // more than MAX_SLACK; a per-lane check and one ballot decide that, and
         // the exact chunk max (two cross-lane reductions) is only taken then.
-        // Wave dh == 0 of the pair publishes the bf16 weights and the factor
-        // that rescales the accumulators (1 when the max stayed).
+        // Both waves of the pair hold the same scores and take the same max
+        // decision; each then forms the bf16 weights of one row tile (wave dh:
+        // rows 16 dh + 4 g + i) and publishes them in its half of the tile's
+        // weight slot, so lsum holds the wave's row tile only (the epilogue
+        // adds the pair's two).  Wave dh == 0 publishes the factor that
+        // rescales the accumulators (1 when the max stayed).
 #pragma unroll
         for (int t = 0; t < HT; ++t) {
             float sv[8];
@@ -1014,25 +1018,27 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             }
             // The weights enter the value product as bf16; the denominator sums
             // the same rounded weights, so numerator and denominator agree.
-            float pv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(sv[e] - m[t]);
-            const u32x4_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3]),
-                                pack2_bf16(pv[4], pv[5]), pack2_bf16(pv[6], pv[7])};
-            float psum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                psum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
-            lsum[t] += psum;
-            if (dh == 0) {
-                pbuf[hq * HT + t][lane] = pw;
-                if (g == 0) abuf[hq * HT + t][li] = alpha;
+            float own[4];  // this wave's row tile (separate copies: a select, not an index)
+            if (dh) {
+                own[0] = sv[4], own[1] = sv[5], own[2] = sv[6], own[3] = sv[7];
+            } else {
+                own[0] = sv[0], own[1] = sv[1], own[2] = sv[2], own[3] = sv[3];
             }
+            float pv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[e] = exp2_fast(own[e] - m[t]);
+            const u32x2_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3])};
+            lsum[t] += __uint_as_float(pw[0] << 16) + __uint_as_float(pw[0] & 0xffff0000u) +
+                       __uint_as_float(pw[1] << 16) + __uint_as_float(pw[1] & 0xffff0000u);
+            *(LDS_AS u32x2_t *)((LDS_AS uint8_t *)&pbuf[hq * HT + t][lane] + 8 * dh) = pw;
+            if (dh == 0 && g == 0) abuf[hq * HT + t][li] = alpha;
         }
     }
 
     // a7 / a8: epilogue.  The last chunk's PV, then each pair publishes the
-    // running max and total denominator of its heads for every wave.
+    // running max and total denominator of its heads for every wave (the
+    // second wave's half of the denominator passes through red, free until
+    // store_outputs).
     static_assert(HWG * D * 2 <= NBUF * KC * RS, "output staging fits in the ring");
     __syncthreads();
     if (nchunks > 0) pv_chunk(nchunks - 1);
@@ -1042,12 +1048,18 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
         const float ltot = sum_rows4(lsum[t]);
-        if (dh == 0 && g == 0) {
-            mh[hq * HW + 16 * t + li] = m[t];
-            lh[hq * HW + 16 * t + li] = ltot;
+        if (g == 0) {
+            if (dh == 0) {
+                mh[hq * HW + 16 * t + li] = m[t];
+                lh[hq * HW + 16 * t + li] = ltot;
+            } else {
+                red[hq * HW + 16 * t + li] = ltot;
+            }
         }
     }
     __syncthreads();  // every wave is done with the ring; reuse it for staging
+    if (tid < HWG) lh[tid] += red[tid];
+    __syncthreads();
     store_outputs<D, NW, NTL>(p, o, mh, lh, red, qi, s, hg, (LDS_AS uint8_t *)&tile[0][0]);
 }
 
