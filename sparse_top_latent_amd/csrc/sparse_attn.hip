@@ -624,7 +624,9 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 
     __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][KC * RS];
     __shared__ __attribute__((aligned(16))) f32x4_t xbuf[NW][2 * HT][64];  // partial scores
-    __shared__ __attribute__((aligned(16))) u32x4_t pbuf[NTL][64];         // bf16 weights per head tile
+    // bf16 weights per head tile and row tile (each wave writes 8 contiguous
+    // bytes per lane: free of bank conflicts)
+    __shared__ __attribute__((aligned(16))) u32x2_t pbuf[NTL][2][64];
     __shared__ float abuf[NTL][16];                                        // rescale factors
     __shared__ int32_t cnt[NW];
     extern __shared__ int32_t list[];  // the compacted list (K entries, dynamic)
@@ -837,7 +839,8 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         float al[NTL];
 #pragma unroll
         for (int t = 0; t < NTL; ++t) {
-            pb[t] = __builtin_bit_cast(bf16x8_t, pbuf[t][lane]);
+            const u32x2_t w0 = pbuf[t][0][lane], w1 = pbuf[t][1][lane];
+            pb[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
             al[t] = abuf[t][li];
         }
         constexpr int PVP = NU < 4 ? NU : 4;
@@ -988,9 +991,9 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         // the exact chunk max (two cross-lane reductions) is only taken then.
         // Both waves of the pair hold the same scores and take the same max
         // decision; each then forms the bf16 weights of one row tile (wave dh:
-        // rows 16 dh + 4 g + i) and publishes them in its half of the tile's
-        // weight slot, so lsum holds the wave's row tile only (the epilogue
-        // adds the pair's two).  Wave dh == 0 publishes the factor that
+        // rows 16 dh + 4 g + i) and publishes them as that row tile's
+        // weights, so lsum holds the wave's row tile only (the epilogue adds
+        // the pair's two).  Wave dh == 0 publishes the factor that
         // rescales the accumulators (1 when the max stayed).
 #pragma unroll
         for (int t = 0; t < HT; ++t) {
@@ -1030,7 +1033,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             const u32x2_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3])};
             lsum[t] += __uint_as_float(pw[0] << 16) + __uint_as_float(pw[0] & 0xffff0000u) +
                        __uint_as_float(pw[1] << 16) + __uint_as_float(pw[1] & 0xffff0000u);
-            *(LDS_AS u32x2_t *)((LDS_AS uint8_t *)&pbuf[hq * HT + t][lane] + 8 * dh) = pw;
+            pbuf[hq * HT + t][dh][lane] = pw;
             if (dh == 0 && g == 0) abuf[hq * HT + t][li] = alpha;
         }
     }
