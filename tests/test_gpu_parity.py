@@ -226,6 +226,29 @@ def test_one_workspace_serves_many_calls(ref):
         assert_close(got.astype(np.float64), exp, f"shared workspace B={B} S={S}")
 
 
+@pytest.mark.parametrize("S", [4, 6])
+def test_combine_ignores_stale_workspace_slots(ref, S):
+    # queries with 640 / 20 / 0 / 200 / 1 valid entries use 4 / 1 / 1 / 2 / 1
+    # of the S split slots; the merge reads every slot's partial and scalars
+    # before the plan entry arrives and masks the ones the plan leaves out, so
+    # a workspace filled with NaN bits (0xFF bytes) must not reach the output.
+    # H = 41 leaves lanes past the last output row in the merge's last block.
+    torch = torch_mod()
+    from sparse_top_latent_amd import api
+    w = wl.make_random(460 + S, 5, 1, 41, 512, 700, 640, p_unused=0.0)
+    idx = w.idxs.copy()
+    for b, n in enumerate((640, 20, 0, 200, 1)):
+        idx[b, 0, n:] = -1
+    q, kv, sk, di = to_dev(w, idx)
+    ws = torch.full((api.workspace_bytes(q, kv, di, S),), 0xFF, dtype=torch.uint8, device=q.device)
+    for rep in range(2):
+        out = api.sparse_attn(q, kv, sk, di, w.scale, num_splits=S, workspace=ws)
+        torch.cuda.synchronize()
+        got = wl.bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+        assert_close(got, ref(w.q, w.kv_host(), w.sink, idx, w.scale), f"stale workspace S={S} call {rep}")
+        ws.fill_(0xFF)
+
+
 def test_bitwise_deterministic():
     w = wl.make_decode(B=8)
     for S in (1, 4):
