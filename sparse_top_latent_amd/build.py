@@ -17,6 +17,12 @@ HIPCC_FLAGS = [
     # MFMA results stay in arch VGPRs: the softmax rescale touches the output
     # accumulators with VALU ops, which cannot read AGPRs
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # every loop marked for unrolling is unrolled: the QK^T loops are sized
+    # before their per-step row-request branches fold to constants, and the
+    # default limit left the FP4 builds' loops rolled, indexing the operand
+    # arrays through select chains (the 32-head FP4 decode kernel ran 37x
+    # slower than its bf16 build)
+    "-mllvm", "-pragma-unroll-threshold=65536",
     "-Wall", "-Wno-unused-function",
 ]
 
