@@ -35,6 +35,10 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    # a rolled operand loop indexes register arrays through select chains
+    # (tens of times slower); every loop marked for unrolling must unroll
+    if "loop not unrolled" in res.stderr:
+        raise RuntimeError("hipcc left a loop marked for unrolling rolled:\n" + res.stderr)
     if verbose:
         print(res.stderr)
     os.replace(tmp, LIB)
