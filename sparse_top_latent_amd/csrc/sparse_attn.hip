@@ -1491,21 +1491,30 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
         }
     }
 
-    // Rounds 0 and 1 are requested from the raw list before the compaction
-    // (entries that are not rows are not fetched); afterwards only the rows
-    // whose number changed are requested again.  A later load into the same
-    // registers returns after the earlier one.
+    // Rounds 0 and 1.  bf16 build: requested after the compaction, every load
+    // unconditional (a round past the list reads q's first 1 KB, in bounds,
+    // and is never used), so that the compiler's count lets the first round's
+    // write wait for round 0 alone.  Requesting them from the raw list before
+    // the compaction held every wave in row-request issue (~3300 cycles for
+    // 12 rows each) ahead of the compaction's barriers, and the conditional
+    // re-requests made the first write wait for both rounds.  FP4 build (row
+    // loads are lane-conditional there anyway): requested from the raw list
+    // before the compaction (entries that are not rows are not fetched), and
+    // afterwards only the rows whose number changed again; a later load into
+    // the same registers returns after the earlier one.
     u32x4_t rg[2][RPW];
     int spec[2][RPW];
+    if constexpr (FP4) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int k = 0; k < RPW; ++k) {
-            const int e = RR * r + RPW * wid + k;
-            const int v = __builtin_amdgcn_readfirstlane(e < p.K ? list[e] : -1);
-            spec[r][k] = v >= 0 && (int64_t)v < p.N ? v : -1;
-            if (spec[r][k] >= 0) load_row(spec[r][k], rg[r][k]);
-        }
+            for (int k = 0; k < RPW; ++k) {
+                const int e = RR * r + RPW * wid + k;
+                const int v = __builtin_amdgcn_readfirstlane(e < p.K ? list[e] : -1);
+                spec[r][k] = v >= 0 && (int64_t)v < p.N ? v : -1;
+                if (spec[r][k] >= 0) load_row(spec[r][k], rg[r][k]);
+            }
+    }
     // a1
     const int n = compact_list<NT>((const LDS_AS int32_t *)&list[0], p.K, p.N, list, cnt);
     const int nr = (n + RR - 1) / RR;
@@ -1515,14 +1524,28 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
         const int e = RR * r + RPW * wid + (lane % RPW);
         return list[e < n ? e : RR * r];
     };
+    if constexpr (FP4) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        if (r < nr) {
-            const int rows = round_rows(r);
+        for (int r = 0; r < 2; ++r) {
+            if (r < nr) {
+                const int rows = round_rows(r);
+#pragma unroll
+                for (int k = 0; k < RPW; ++k) {
+                    const int rw = __builtin_amdgcn_readlane(rows, k);
+                    if (rw != spec[r][k]) load_row(rw, rg[r][k]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int rows = r < nr ? round_rows(r) : 0;
 #pragma unroll
             for (int k = 0; k < RPW; ++k) {
                 const int rw = __builtin_amdgcn_readlane(rows, k);
-                if (rw != spec[r][k]) load_row(rw, rg[r][k]);
+                const u32x4_t *src = r < nr ? (const u32x4_t *)((rw < p.W ? kva : kvb2) + (int64_t)rw * D) + lane
+                                            : (const u32x4_t *)p.q + lane;
+                rg[r][k] = *src;
             }
         }
     }
