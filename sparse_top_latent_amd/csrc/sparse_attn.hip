@@ -1384,7 +1384,7 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 // (they share an XCD, so the repeats come from L2).
 //
 // FP4 build (f2): a row of the second source is its record (rec2 bytes, one
-// load by the first rec2/16 lanes), written into its padded LDS row where
+// load, the first rec2/16 lanes' bytes kept), written into its padded LDS row where
 // expand_fp4_own expects it and expanded there in place by the wave that wrote
 // it, before the round's barrier; the bf16 rows the kernel then reads are the
 // ones the bf16 build reads, so both builds agree bit for bit.
@@ -1444,14 +1444,16 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
     const uint16_t *kva = p.kv + (int64_t)b * p.rows_a * D;
     const uint16_t *kvb2 = p.kv2 + ((int64_t)b * p.rows_b - p.W) * D;
     const uint8_t *recb = (const uint8_t *)p.kv2 + ((int64_t)b * p.rows_b - p.W) * p.rec2;
-    // a2: this lane's 16 bytes of row j (one wave instruction per row); FP4
-    // build, j >= W: of its record (lanes below rec2/16)
-    auto load_row = [&](int j, u32x4_t &dst) {
-        if (!FP4 || j < p.W)
-            dst = *((const u32x4_t *)((j < p.W ? kva : kvb2) + (int64_t)j * D) + lane);
-        else if (lane * 16 < p.rec2)
-            dst = *(const u32x4_t *)(recb + (int64_t)j * p.rec2 + lane * 16);
+    // a2: where this lane's 16 bytes of row j are (one wave instruction per
+    // row); FP4 build, j >= W: of its record, lanes past the record reading
+    // its last 16 bytes again (unused).  Every lane loads, so no load sits in a
+    // lane-dependent branch and the compiler can count them.
+    auto row_src = [&](int j) {
+        if (FP4 && j >= p.W)
+            return (const u32x4_t *)(recb + (int64_t)j * p.rec2 + (lane * 16 < p.rec2 ? lane * 16 : p.rec2 - 16));
+        return (const u32x4_t *)((j < p.W ? kva : kvb2) + (int64_t)j * D) + lane;
     };
+    auto load_row = [&](int j, u32x4_t &dst) { dst = *row_src(j); };
     // row j into position r of a round buffer (a record where expand_fp4_own reads it)
     auto write_row = [&](LDS_AS uint8_t *Lb, int r, int j, const u32x4_t &v) {
         if (!FP4 || j < p.W)
@@ -1491,31 +1493,13 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
         }
     }
 
-    // Rounds 0 and 1.  bf16 build: requested after the compaction, every load
-    // unconditional (a round past the list reads q's first 1 KB, in bounds,
-    // and is never used), so that the compiler's count lets the first round's
-    // write wait for round 0 alone.  Requesting them from the raw list before
-    // the compaction held every wave in row-request issue (~3300 cycles for
-    // 12 rows each) ahead of the compaction's barriers, and the conditional
-    // re-requests made the first write wait for both rounds.  FP4 build (row
-    // loads are lane-conditional there anyway): requested from the raw list
-    // before the compaction (entries that are not rows are not fetched), and
-    // afterwards only the rows whose number changed again; a later load into
-    // the same registers returns after the earlier one.
-    u32x4_t rg[2][RPW];
-    int spec[2][RPW];
-    if constexpr (FP4) {
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int k = 0; k < RPW; ++k) {
-                const int e = RR * r + RPW * wid + k;
-                const int v = __builtin_amdgcn_readfirstlane(e < p.K ? list[e] : -1);
-                spec[r][k] = v >= 0 && (int64_t)v < p.N ? v : -1;
-                if (spec[r][k] >= 0) load_row(spec[r][k], rg[r][k]);
-            }
-    }
-    // a1
+    // a1, then rounds 0 and 1, every load unconditional (a round past the
+    // list reads q's first 1 KB, in bounds, and is never used), so that the
+    // compiler's count lets the first round's write wait for round 0 alone.
+    // Requesting them from the raw list before the compaction held every wave
+    // in row-request issue (~3300 cycles for 12 rows each) ahead of the
+    // compaction's barriers, and the conditional re-requests after it made
+    // the first write wait for both rounds.
     const int n = compact_list<NT>((const LDS_AS int32_t *)&list[0], p.K, p.N, list, cnt);
     const int nr = (n + RR - 1) / RR;
     // the wave's rows of round r (lane k < RPW holds its k-th); positions
@@ -1524,29 +1508,14 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
         const int e = RR * r + RPW * wid + (lane % RPW);
         return list[e < n ? e : RR * r];
     };
-    if constexpr (FP4) {
+    u32x4_t rg[2][RPW];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (r < nr) {
-                const int rows = round_rows(r);
+    for (int r = 0; r < 2; ++r) {
+        const int rows = r < nr ? round_rows(r) : 0;
 #pragma unroll
-                for (int k = 0; k < RPW; ++k) {
-                    const int rw = __builtin_amdgcn_readlane(rows, k);
-                    if (rw != spec[r][k]) load_row(rw, rg[r][k]);
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int rows = r < nr ? round_rows(r) : 0;
-#pragma unroll
-            for (int k = 0; k < RPW; ++k) {
-                const int rw = __builtin_amdgcn_readlane(rows, k);
-                const u32x4_t *src = r < nr ? (const u32x4_t *)((rw < p.W ? kva : kvb2) + (int64_t)rw * D) + lane
-                                            : (const u32x4_t *)p.q + lane;
-                rg[r][k] = *src;
-            }
+        for (int k = 0; k < RPW; ++k) {
+            const int rw = __builtin_amdgcn_readlane(rows, k);
+            rg[r][k] = *(r < nr ? row_src(rw) : (const u32x4_t *)p.q + lane);
         }
     }
 
