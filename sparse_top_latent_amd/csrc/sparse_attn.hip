@@ -1920,28 +1920,67 @@ __device__ void find_digit(const int *hist, int need, int *ws, int *sh) {
     __syncthreads();
 }
 
+// Histogram slot of digit b in the register kernel: the 16-byte groups of
+// each 32-bin block are permuted by the block number, so that the one wave
+// that reads the whole histogram (lane l one block, a 16-byte group per
+// instruction) spreads every instruction's 64 lanes over all 32 banks.
+__device__ __forceinline__ int bin_slot(int b) { return b ^ (((b >> 5) & 7) << 2); }
+
+// find_digit for a swizzled histogram, done by wave 0 alone: lane l sums the
+// 32 bins of block 63 - l (so lower lanes hold higher digits), one scan over
+// the wave gives the count above each block, and the block where the count
+// reaches `need` is scanned again bin by bin, one bin per lane.  Leaves the
+// digit, what is still needed within it and its bin count in sh[0..2].  Every
+// thread calls it; it ends with a barrier.
+__device__ void find_digit_wave(const int *hist, int need, int *sh) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x, blk = 63 - lane;
+        int sum = 0;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int4 v = *(const int4 *)&hist[32 * blk + 4 * (g ^ (blk & 7))];
+            sum += v.x + v.y + v.z + v.w;
+        }
+        const int above = wave_inclusive_scan(sum) - sum;
+        // exactly one block holds the crossing (1 <= need <= the total)
+        const uint64_t cross = __ballot(above < need && above + sum >= need);
+        if (cross != 0) {
+            const int cl = __ffsll((unsigned long long)cross) - 1;
+            const int cabove = __builtin_amdgcn_readlane(above, cl);
+            const int bin = 32 * (63 - cl) + 31 - (lane & 31);  // descending within the block
+            const int hv = lane < 32 ? hist[bin_slot(bin)] : 0;
+            const int upto = cabove + wave_inclusive_scan(hv);
+            if (lane < 32 && upto - hv < need && upto >= need) {
+                sh[0] = bin;
+                sh[1] = need - (upto - hv);
+                sh[2] = hv;
+            }
+        }
+    }
+    __syncthreads();
+}
+
 // One workgroup per query, KPT keys per thread in registers (thread t holds
 // positions t*KPT .. t*KPT+KPT-1, so the workgroup covers NT*KPT positions).
 // A radix select over the keys narrows the key of the k-th best down to a
 // prefix; it stops early once every key that matches the prefix is taken.
 // Then one scan of the packed counts (keys above the prefix, keys equal to it)
-// gives each thread its output position.  Per key the work is branch-free:
-// keys outside the prefix add to a per-lane spare counter instead of a bin,
-// and each thread writes its picks in index order into an LDS row (non-picks
-// to its spare slot), which the workgroup then copies out; k above the LDS
-// row stores the picks directly.
-constexpr int TOPK_STAGE = TOPK_BINS;  // picks staged in LDS up to this k
+// gives each thread its output position, and each thread stores its picks
+// there in index order.  The chain is short on purpose (it bounds the kernel
+// at one row per workgroup): both histograms are cleared while the keys load,
+// one wave finds each digit, and the scan takes one barrier.
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void topk_reg_kernel(const float *__restrict__ scores,
                                                       const int32_t *__restrict__ lens, int32_t C,
                                                       int32_t k, int32_t offset, int32_t *out,
                                                       int64_t out_stride) {
     static_assert(NT >= 64 && TOPK_BINS % NT == 0 && KPT % 4 == 0, "bins per thread, float4 loads");
-    // two histograms used by alternate passes, each with 64 spare counters
-    __shared__ __attribute__((aligned(16))) int hist[2][TOPK_BINS + 64];
+    static_assert(TOPK_BINS == 64 * 32, "one wave reads the histogram, 32 bins per lane");
+    // two histograms used by alternate passes
+    __shared__ __attribute__((aligned(16))) int hist[2][TOPK_BINS];
     __shared__ int ws[NT / 64];
     __shared__ int sh[3];
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t q = blockIdx.x;
     const float *s = scores + q * C;
     int L = lens != nullptr ? lens[q] : C;
@@ -1953,6 +1992,8 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float *__restrict__ 
         for (int j = tid; j < L; j += NT) o[j] = j + offset;
         return;
     }
+#pragma unroll
+    for (int j = 0; j < TOPK_BINS / NT; ++j) hist[0][tid + j * NT] = 0, hist[1][tid + j * NT] = 0;
     const int base = tid * KPT;
     const int nv = L - base < 0 ? 0 : (L - base > KPT ? KPT : L - base);
     const bool vec = ((C & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
@@ -1968,18 +2009,14 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float *__restrict__ 
 #pragma unroll
         for (int j = 0; j < KPT; ++j) key[j] = j < nv ? score_key(s[base + j]) : 0u;
     }
-#pragma unroll
-    for (int j = 0; j < TOPK_BINS / NT; ++j) hist[0][tid + j * NT] = 0;
     __syncthreads();
 
     // pass 0: every key counts, by its top digit
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) atomicAdd(&hist[0][key[j] >> 21], 1);
-    if (tid == 0 && NT * KPT > L) atomicAdd(&hist[0][0], L - NT * KPT);
-#pragma unroll
-    for (int j = 0; j < TOPK_BINS / NT; ++j) hist[1][tid + j * NT] = 0;
+    for (int j = 0; j < KPT; ++j) atomicAdd(&hist[0][bin_slot(key[j] >> 21)], 1);
+    if (tid == 0 && NT * KPT > L) atomicAdd(&hist[0][bin_slot(0)], L - NT * KPT);
     __syncthreads();
-    find_digit<NT>(hist[0], kk, ws, sh);
+    find_digit_wave(hist[0], kk, sh);
     uint32_t prefix = (uint32_t)sh[0] << 21, mask = 2047u << 21;
     int need = sh[1];  // still to take among the keys that match the prefix
 #pragma unroll 1
@@ -1987,18 +2024,19 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float *__restrict__ 
         const int shift = digit_shift(pass);
         const uint32_t dm = digit_mask(pass);
         int *hc = hist[pass & 1];
+        // only keys that match the prefix count (a few percent of them after
+        // pass 0): an LDS atomic costs per active lane, so the rest sit out
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-            const bool in = j < nv && (key[j] & mask) == prefix;
-            atomicAdd(&hc[in ? (int)((key[j] >> shift) & dm) : TOPK_BINS + lane], 1);
+            if (j < nv && (key[j] & mask) == prefix) atomicAdd(&hc[bin_slot((int)((key[j] >> shift) & dm))], 1);
         }
-        // the other histogram was last read before the previous barrier
+        // pass 2 counts into histogram 0, last read before the previous barrier
         if (pass < 2) {
 #pragma unroll
-            for (int j = 0; j < TOPK_BINS / NT; ++j) hist[(pass + 1) & 1][tid + j * NT] = 0;
+            for (int j = 0; j < TOPK_BINS / NT; ++j) hist[0][tid + j * NT] = 0;
         }
         __syncthreads();
-        find_digit<NT>(hc, need, ws, sh);
+        find_digit_wave(hc, need, sh);
         prefix |= (uint32_t)sh[0] << shift;
         mask |= dm << shift;
         need = sh[1];
@@ -2013,35 +2051,25 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float *__restrict__ 
         gt += j < nv && m > prefix;
         eq += j < nv && m == prefix;
     }
-    int tot;
-    const int before = block_exclusive_scan<NT>((eq << 16) | gt, ws, &tot);
+    const int v = (eq << 16) | gt;
+    const int incl = wave_inclusive_scan(v);
+    if (lane == 63) ws[wid] = incl;
+    __syncthreads();
+    int before = incl - v;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) before += w < wid ? ws[w] : 0;
     const int eq_before = before >> 16, gt_before = before & 0xFFFF;
     int take_eq = need - eq_before;
     take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
     int pos = gt_before + (eq_before < need ? eq_before : need);
-    if (kk <= TOPK_STAGE) {  // uniform
-        int *row = hist[0];  // free: the passes are over (barrier in the scan)
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const uint32_t m = key[j] & mask;
-            const bool tie = j < nv && m == prefix && take_eq > 0;
-            const bool pick = (j < nv && m > prefix) || tie;
-            row[pick && pos < kk ? pos : TOPK_BINS + lane] = base + j + offset;
-            pos += pick;
-            take_eq -= tie;
-        }
-        __syncthreads();
-        for (int j = tid; j < kk; j += NT) o[j] = row[j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const uint32_t m = key[j] & mask;
-            if (j < nv && (m > prefix || (m == prefix && take_eq > 0))) {
-                if (m == prefix) --take_eq;
-                if (pos < kk) o[pos] = base + j + offset;
-                ++pos;
-            }
-        }
+    for (int j = 0; j < KPT; ++j) {
+        const uint32_t m = key[j] & mask;
+        const bool tie = j < nv && m == prefix && take_eq > 0;
+        const bool pick = (j < nv && m > prefix) || tie;
+        if (pick && pos < kk) o[pos] = base + j + offset;
+        pos += pick;
+        take_eq -= tie;
     }
 }
 
