@@ -1394,8 +1394,12 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
 // (ordinary 16-byte loads, the compiler tracks them) while round i is
 // computed, and writes round i into one of three LDS round buffers, so no LDS
 // holds rows in flight.  (The compiler's waits before those writes cover every
-// load in flight, round i + 1's too; a variant with a fixed count of loads per
-// round, which let it wait for round i alone, measured no faster.)  Iteration i: round i's rows go to LDS, one barrier, then
+// load in flight, round i + 1's too.  Issuing every round's loads
+// unconditionally, past the list the last round's rows again, lets it wait for
+// round i alone, but measured slower on MI355X: 10.7 against 9.7 us for 64
+// window-only lists, and slower at every list length up to 512: the extra
+// rounds of loads and the extra barrier at the end cost more.)
+// Iteration i: round i's rows go to LDS, one barrier, then
 //   - waves 0..2 (the scorers) each take one 16-row block of round i: S^T over
 //     all of d (q of the 16 heads in registers), the block's softmax weights
 //     as bf16, published with the block's reference max and weight sum;
