@@ -1107,12 +1107,15 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     const int bid = blockIdx.x;
     const int unit = unit_of(bid, p.units, p.bs);
     if (unit < 0) return;
-    const int s = unit % p.S;
-    const int hg = (unit / p.S) % p.HG;
-    const int qi = unit / (p.S * p.HG);
-    const int b = qi / p.T;
+    // workgroup-uniform: kept in scalar registers (the divisions run on the
+    // vector unit), so the row and record base addresses below are scalar too
+    const int s = __builtin_amdgcn_readfirstlane(unit % p.S);
+    const int hg = __builtin_amdgcn_readfirstlane((unit / p.S) % p.HG);
+    const int qi = __builtin_amdgcn_readfirstlane(unit / (p.S * p.HG));
+    const int b = __builtin_amdgcn_readfirstlane(qi / p.T);
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // the wave number is uniform: in a scalar register, so are the offsets it sets
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hq = wid >> 1;      // pair
     const int w = wid & 1;        // own head tile (QK^T, softmax) and half of d (PV)
     const int g = lane >> 4, li = lane & 15;
@@ -1151,7 +1154,9 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     static_assert(IPW % 4 == 0, "rows are requested four at a time");
     auto rows_of = [&](int c) {
         const int e0 = lo + c * KC;
-        const int e = e0 + wid * IPW + lane % IPW;
+        int ln = lane;  // formed here, not held across the loop (see stage_pair)
+        asm volatile("" : "+v"(ln));
+        const int e = e0 + wid * IPW + ln % IPW;
         return list[e < hi ? e : e0];
     };
     // this wave's k-th row of chunk c: a bf16 row, or (FP4 build, rows >= W)
@@ -1167,15 +1172,24 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
             lds_dma16_s(recb + (int64_t)row * p.rec2, lane * 16, dst + ((k & 1) ? 0 : RS - p.rec2));
         }
     };
-    // FP4 build: rows k (even) and k + 1; two records share one instruction
+    // FP4 build: rows k (even) and k + 1; two records share one instruction,
+    // addressed from the lower record (a scalar base) plus a 32-bit lane
+    // offset, so that no per-lane 64-bit address stays live across the loop
     auto stage_pair = [&](int c, int rows, int k) {
         const int r0 = __builtin_amdgcn_readlane(rows, k), r1 = __builtin_amdgcn_readlane(rows, k + 1);
-        if (r0 >= p.W && r1 >= p.W) {
+        const int rlo = r0 < r1 ? r0 : r1;
+        const int64_t span = (int64_t)(r0 < r1 ? r1 - r0 : r0 - r1) * p.rec2;
+        if (r0 >= p.W && r1 >= p.W && span < 0x7FFFFFFF - 1024) {
             const int nl = p.rec2 / 16;  // lanes per record
             LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NB][0] + (wid * IPW + k) * RS + RS - p.rec2;
-            const uint8_t *src = lane < nl ? recb + (int64_t)r0 * p.rec2 + lane * 16
-                                           : recb + (int64_t)r1 * p.rec2 + (lane - nl) * 16;
-            if (lane < 2 * nl) lds_dma16_nt(src, (LDS_AS void *)dst);
+            // the lane's offset is formed here, not hoisted out of the chunk
+            // loop (a register held across the loop spilled, and each reload
+            // waited for every row request in flight)
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const uint32_t voff = ln < nl ? (uint32_t)((r0 - rlo) * p.rec2 + ln * 16)
+                                          : (uint32_t)((r1 - rlo) * p.rec2 + (ln - nl) * 16);
+            if (ln < 2 * nl) lds_dma16_s(recb + (int64_t)rlo * p.rec2, voff, (LDS_AS void *)dst);
         } else {
             stage_one(c, rows, k);
             stage_one(c, rows, k + 1);
