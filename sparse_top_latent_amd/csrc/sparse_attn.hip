@@ -639,12 +639,13 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     const int bid = blockIdx.x;
     const int unit = unit_of(bid, p.units, p.bs);
     if (unit < 0) return;
-    const int s = unit % p.S;
-    const int hg = (unit / p.S) % p.HG;
-    const int qi = unit / (p.S * p.HG);
-    const int b = qi / p.T;
+    // workgroup- and wave-uniform values in scalar registers
+    const int s = __builtin_amdgcn_readfirstlane(unit % p.S);
+    const int hg = __builtin_amdgcn_readfirstlane((unit / p.S) % p.HG);
+    const int qi = __builtin_amdgcn_readfirstlane(unit / (p.S * p.HG));
+    const int b = __builtin_amdgcn_readfirstlane(qi / p.T);
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hq = wid >> 1;      // head group of this wave
     const int dh = wid & 1;       // half of d this wave covers
     const int g = lane >> 4;      // 16-lane block of the wave
