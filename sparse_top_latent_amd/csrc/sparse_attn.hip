@@ -1453,10 +1453,11 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
 
     const int unit = unit_of(blockIdx.x, p.units, p.bs);
     if (unit < 0) return;
-    const int hg = unit % p.HG;
-    const int qi = unit / p.HG;
-    const int b = qi / p.T;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // workgroup- and wave-uniform values in scalar registers
+    const int hg = __builtin_amdgcn_readfirstlane(unit % p.HG);
+    const int qi = __builtin_amdgcn_readfirstlane(unit / p.HG);
+    const int b = __builtin_amdgcn_readfirstlane(qi / p.T);
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, li = lane & 15;
     const int h = hg * 16 + li;  // head of this lane (QK^T columns, softmax, outputs)
     const bool scorer = wid < NB;
