@@ -218,7 +218,7 @@ __device__ int compact_list(const LDS_AS int32_t *lst, int K, int64_t N, int32_t
                             int32_t *cnt) {
     constexpr int NWV = NT / 64;
     constexpr int MAXR = (LIST_CAP + NT - 1) / NT;  // rounds of 64 per wave, at most
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int seg = ((K + NWV - 1) / NWV + 63) / 64 * 64;
     const int k0 = wid * seg;
     int v[MAXR];
@@ -394,7 +394,7 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
     constexpr int DW = D / NW;
     constexpr int NU = DW / 16;
     constexpr int C16 = D / 8;  // 16-byte chunks per 16-bit row
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, li = lane & 15;
     const int hbase = hg * HWG;
     float inv[NTL];
