@@ -337,6 +337,31 @@ __device__ __forceinline__ void lds_dma16x4_s(const uint8_t *s0, const uint8_t *
                  : "memory", "m0");
 }
 
+// The saddr forms with the non-temporal hint (rows read once).
+__device__ __forceinline__ void lds_dma16_s_nt(const void *sbase, uint32_t voff,
+                                               const LDS_AS void *lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+}
+template <int RS>
+__device__ __forceinline__ void lds_dma16x4_s_nt(const uint8_t *s0, const uint8_t *s1, const uint8_t *s2,
+                                                 const uint8_t *s3, uint32_t voff, const LDS_AS void *lds_base) {
+    static_assert(3 * RS < 4096, "row offsets fit the instruction's offset field");
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %1 nt\n\t"
+                 "global_load_lds_dwordx4 %0, %2 offset:%6 nt\n\t"
+                 "global_load_lds_dwordx4 %0, %3 offset:%7 nt\n\t"
+                 "global_load_lds_dwordx4 %0, %4 offset:%8 nt"
+                 :
+                 : "v"(voff), "s"(s0), "s"(addr_less(s1, RS)), "s"(addr_less(s2, 2 * RS)),
+                   "s"(addr_less(s3, 3 * RS)), "s"(m0), "n"(RS), "n"(2 * RS), "n"(3 * RS)
+                 : "memory", "m0");
+}
+
 // Same with 4 bytes per lane (landing at lds_base + 4 * lane).
 __device__ __forceinline__ void lds_dma4(const void *gptr, const LDS_AS void *lds_base) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
@@ -698,11 +723,17 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     // odd one, so a pair of records shares one instruction (see expand_fp4_own).
     // The lambdas return the number of DMA instructions they issued.
     static_assert(IPW % 4 == 0, "rows are requested four at a time");
+    // Row numbers and W are below 2^31 (a row holds at least 256 bytes), so
+    // the source test is a 32-bit scalar compare and a row's address a scalar
+    // base plus the lane's 16-byte offset (saddr form).
+    const int Wc = (int)(p.W < 0x7FFFFFFF ? p.W : 0x7FFFFFFF);
+    auto row_base = [&](int rw) {
+        return (const uint8_t *)((rw < Wc ? kva : kvb2) + (int64_t)rw * D);
+    };
     auto dma_row = [&](int c, int k, int rw) {
         LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (wid * IPW + k) * RS;
         if (!FP4 || rw < p.W) {
-            if (CPR == 64 || lane < CPR)
-                lds_dma16_nt((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8, (LDS_AS void *)dst);
+            if (CPR == 64 || lane < CPR) lds_dma16_s_nt(row_base(rw), lane * 16, (LDS_AS void *)dst);
         } else if (lane * 16 < p.rec2) {
             lds_dma16_nt(recb + (int64_t)rw * p.rec2 + lane * 16,
                          (LDS_AS void *)(dst + ((k & 1) ? 0 : RS - p.rec2)));
@@ -727,10 +758,8 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             return dma_pair(c, k0, r0, r1) + dma_pair(c, k0 + 2, r2, r3);
         } else {
             LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NBUF][0] + (wid * IPW + k0) * RS;
-            auto src = [&](int rw) {
-                return (const uint8_t *)((rw < p.W ? kva : kvb2) + (int64_t)rw * D + lane * 8);
-            };
-            if (CPR == 64 || lane < CPR) lds_dma16x4_nt<RS>(src(r0), src(r1), src(r2), src(r3), dst);
+            if (CPR == 64 || lane < CPR)
+                lds_dma16x4_s_nt<RS>(row_base(r0), row_base(r1), row_base(r2), row_base(r3), lane * 16, dst);
             return 4;
         }
     };
