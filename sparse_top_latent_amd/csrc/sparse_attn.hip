@@ -1189,13 +1189,16 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         const int e = e0 + wid * IPW + ln % IPW;
         return list[e < hi ? e : e0];
     };
+    // Row numbers and W are below 2^31 (a row holds at least 256 bytes), so
+    // the source test is a 32-bit scalar compare.
+    const int Wc = (int)(p.W < 0x7FFFFFFF ? p.W : 0x7FFFFFFF);
     // this wave's k-th row of chunk c: a bf16 row, or (FP4 build, rows >= W)
     // a record landing at the tail of the row's slot
     auto stage_one = [&](int c, int rows, int k) {
         const int row = __builtin_amdgcn_readlane(rows, k);
         LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NB][0] + (wid * IPW + k) * RS;
-        if (!FP4 || row < p.W) {
-            const uint16_t *src = (row < p.W ? kva : kvb2) + (int64_t)row * D;
+        if (!FP4 || row < Wc) {
+            const uint16_t *src = (row < Wc ? kva : kvb2) + (int64_t)row * D;
             if (CPR == 64 || lane < CPR) lds_dma16_s(src, lane * 16, dst);
         } else if (lane * 16 < p.rec2) {
             // an FP4 record: at the tail of an even row, the head of an odd one
@@ -1209,7 +1212,7 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         const int r0 = __builtin_amdgcn_readlane(rows, k), r1 = __builtin_amdgcn_readlane(rows, k + 1);
         const int rlo = r0 < r1 ? r0 : r1;
         const int64_t span = (int64_t)(r0 < r1 ? r1 - r0 : r0 - r1) * p.rec2;
-        if (r0 >= p.W && r1 >= p.W && span < 0x7FFFFFFF - 1024) {
+        if (r0 >= Wc && r1 >= Wc && span < 0x7FFFFFFF - 1024) {
             const int nl = p.rec2 / 16;  // lanes per record
             LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NB][0] + (wid * IPW + k) * RS + RS - p.rec2;
             // the lane's offset is formed here, not hoisted out of the chunk
@@ -1233,7 +1236,7 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         } else {
             auto src = [&](int k) {
                 const int row = __builtin_amdgcn_readlane(rows, k);
-                return (const uint8_t *)((row < p.W ? kva : kvb2) + (int64_t)row * D);
+                return (const uint8_t *)((row < Wc ? kva : kvb2) + (int64_t)row * D);
             };
             LDS_AS uint8_t *dst = (LDS_AS uint8_t *)&tile[c % NB][0] + (wid * IPW + 4 * q) * RS;
             if (CPR == 64 || lane < CPR)
