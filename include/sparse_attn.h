@@ -52,7 +52,8 @@ extern "C" {
 
 typedef struct ihipStream_t *hipStream_t;
 
-/* Sizes of one call.  B, T >= 0 (zero queries is a no-op); H, D >= 1; N >= 0; K >= 0. */
+/* Sizes of one call.  B, T >= 0 (zero queries is a no-op); H, D >= 1; N >= 0; K >= 0;
+ * B*T*H < 2^31 (output rows are numbered in 32 bits; else SA_ERR_SHAPE). */
 typedef struct sa_dims {
     int32_t B, T, H, D, N, K;
 } sa_dims;

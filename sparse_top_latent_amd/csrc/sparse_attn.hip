@@ -163,10 +163,6 @@ __device__ __forceinline__ int unit_of(int bid, int units, int bs) {
     return u < units ? units - 1 - u : -1;
 }
 
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
-    return __shfl_xor(v, mask, 64);
-}
-
 // Sum and max of x over the lanes l mod 16 + 16k, k = 0..3 (the four 16-lane
 // rows of a wave), returned in every lane: two lane swaps on the VALU
 // (gfx950's v_permlane16_swap and v_permlane32_swap) in place of two LDS
@@ -185,6 +181,35 @@ __device__ __forceinline__ float max_rows4(float x) {
     const float y = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
     const u32x2_t q = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false));
     return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// Max or sum of x over each aligned group of G lanes (G = 16, 32 or 64),
+// returned in every lane of the group, on the VALU: within a 16-lane row by
+// DPP (quad permutes, then the half-row and row mirrors, each pairing every
+// lane with one from the other half of its group), across rows by the lane
+// swaps above.  (Cross-lane shuffles through LDS would take one LDS round
+// trip per step.)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int G, bool MAX>
+__device__ __forceinline__ float group_reduce(float x) {
+    static_assert(G == 16 || G == 32 || G == 64, "rows of 16 lanes");
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    x = op(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = op(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = op(x, dpp_f<0x141>(x));  // row_half_mirror
+    x = op(x, dpp_f<0x140>(x));  // row_mirror
+    if constexpr (G >= 32) {
+        const u32x2_t p = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false));
+        x = op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    if constexpr (G == 64) {
+        const u32x2_t q = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false));
+        x = op(__uint_as_float(q[0]), __uint_as_float(q[1]));
+    }
+    return x;
 }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -1746,7 +1771,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                                                       const float *__restrict__ ws_x,
                                                       const int32_t *__restrict__ ws_plan,
                                                       const float *__restrict__ sink,
-                                                      uint16_t *__restrict__ out, int64_t QH,
+                                                      uint16_t *__restrict__ out, int QH,
                                                       int H, int S, int per_xcd,
                                                       const float *__restrict__ rope, int rd,
                                                       int T) {
@@ -1760,16 +1785,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     const int bid = blockIdx.x;
     // reversed blocks per XCD, like the attention kernels' unit order (the
     // partials of a query were written on the XCD that merges them)
-    const int64_t wg = (int64_t)8 * per_xcd - 1 - ((int64_t)(bid & 7) * per_xcd + (bid >> 3));
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    // output rows are numbered in 32 bits (the host keeps B*T*H below 2^31),
+    // so the divisions below are 32-bit ones; the workgroup's numbers are
+    // scalar
+    const int wg = __builtin_amdgcn_readfirstlane(8 * per_xcd - 1 - ((bid & 7) * per_xcd + (bid >> 3)));
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rw = wid * RPW + lane / LPR;   // row within the workgroup
     const int sl = lane % LPR;               // lane within the row
-    const int64_t qh = wg * RWG + rw;
+    const int qh = wg * RWG + rw;
     const bool ok = qh < QH;                  // (no early exit: the row's lanes shuffle)
-    const int64_t qi = ok ? qh / H : 0;
-    const int h = ok ? (int)(qh % H) : 0;
+    const int qi = ok ? qh / H : 0;
+    const int h = ok ? qh - qi * H : 0;
     const int c8 = sl * 8;
-    const int64_t slot0 = qi * S * H + h;    // slot of split j: slot0 + j * H
+    const int64_t slot0 = (int64_t)qi * S * H + h;  // slot of split j: slot0 + j * H
     // a10: the splits this query's list was cut into (the first Sq slots).
     // The first batch of partials and every scalar are requested before Sq
     // arrives (all S slots lie inside the workspace; a slot the plan leaves
@@ -1829,26 +1857,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     float mx = mz;
 #pragma unroll
     for (int k = 0; k < SPL; ++k) mx = fmaxf(mx, mj[k]);
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
+    mx = group_reduce<LPR, true>(mx);
     float L = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
         for (int k = 0; k < SPL; ++k) L += exp2_fast(mj[k] - mx) * lj[k];
     }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) L += shfl_xor_f(L, off);
+    L = group_reduce<LPR, false>(L);
     if (mx != -INFINITY && sink != nullptr) L += exp2_fast(mz - mx);
     const float invL = L > 0.f ? 1.f / L : 0.f;
+    // split j's factor: with a row per wave (LPR = 64, one slot per lane) lane
+    // j holds it and the others read it with a lane read; else through LDS
+    float cj[SPL];
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
         const int j = sl + k * LPR;
-        if (j < S) {
-            const float c = mx != -INFINITY ? exp2_fast(mj[k] - mx) * lj[k] * invL : 0.f;
-            coef[rw][j] = c * xj[k];
-        }
+        const float c = mx != -INFINITY ? exp2_fast(mj[k] - mx) * lj[k] * invL : 0.f;
+        cj[k] = c * xj[k];
+        if (LPR < 64 && j < S) coef[rw][j] = cj[k];
     }
-    __syncthreads();
+    if constexpr (LPR < 64) __syncthreads();
+    auto coef_of = [&](int j) {
+        if constexpr (LPR == 64) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cj[0]), j));
+        else return coef[rw][j];
+    };
 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < S; j0 += SB) {
@@ -1860,7 +1892,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
             if (j0 + j < S) {
-                const float c = coef[rw][j0 + j];
+                const float c = coef_of(j0 + j);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const f32x2_t f = unpack2_f16(v[j][e]);
@@ -1877,7 +1909,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     if (ok) {
         const u32x4_t w = {pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]),
                            pack2_bf16(acc[4], acc[5]), pack2_bf16(acc[6], acc[7])};
-        *(u32x4_t *)(out + qh * D + c8) = w;
+        *(u32x4_t *)(out + (int64_t)qh * D + c8) = w;
     }
 }
 
@@ -2237,6 +2269,8 @@ int check_dims(const sa_dims *d) {
     if (d->B < 0 || d->T < 0 || d->H < 1 || d->D < 1 || d->N < 0 || d->K < 0) return SA_ERR_SHAPE;
     if (d->D != 128 && d->D != 256 && d->D != 512) return SA_ERR_UNSUPPORTED;
     if (d->K > LIST_CAP) return SA_ERR_UNSUPPORTED;
+    // output rows (query, head) are numbered in 32 bits on the device
+    if ((int64_t)d->B * d->T * d->H > 0x7FFFFFFF) return SA_ERR_SHAPE;
     return SA_OK;
 }
 
@@ -2371,7 +2405,7 @@ hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
     const int32_t *wp = (const int32_t *)((const uint8_t *)ws + L.plan_off);
     uint16_t *o = (uint16_t *)out;
 #define SA_COMBINE(DD, SB) \
-    hipLaunchKernelGGL((combine_kernel<DD, SB>), dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, QH, d->H, S, per_xcd, rope, rd, d->T)
+    hipLaunchKernelGGL((combine_kernel<DD, SB>), dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, (int)QH, d->H, S, per_xcd, rope, rd, d->T)
     const bool small = S <= 4;  // one batch of four holds every split
     switch (d->D) {
         case 128: if (small) SA_COMBINE(128, 4); else SA_COMBINE(128, 8); break;

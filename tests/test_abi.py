@@ -106,6 +106,9 @@ def test_dims_errors(L):
     assert fwd(L, d=dims(D=64)) == SA_ERR_UNSUPPORTED
     assert fwd(L, d=dims(D=100)) == SA_ERR_UNSUPPORTED
     assert fwd(L, d=dims(K=2049)) == SA_ERR_UNSUPPORTED
+    # output rows (query, head) are numbered in 32 bits on the device
+    assert fwd(L, d=dims(B=65536, T=512, H=64)) == SA_ERR_SHAPE  # B*T*H = 2^31
+    assert L.sparse_attn_workspace_bytes_splits(dims(B=65536, T=512, H=64), 2) == 0
 
 
 def test_pointer_errors(L):
