@@ -146,7 +146,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // compaction; split 0 records Sq for the combine.
 __device__ __forceinline__ int query_splits(int n, int K, int S) {
     if (S <= 1 || K <= 0) return 1;
-    const int sq = (int)(((int64_t)n * S + K - 1) / K);
+    const int sq = (n * S + K - 1) / K;  // n <= K <= LIST_CAP, S <= MAX_SPLITS: 32 bits suffice
     return sq < 1 ? 1 : (sq > S ? S : sq);
 }
 
@@ -249,6 +249,8 @@ __device__ int compact_list(const LDS_AS int32_t *lst, int K, int64_t N, int32_t
     int v[MAXR];
     uint64_t mask[MAXR];
     int total = 0;
+    // 0 <= v < N as one unsigned 32-bit compare (entries are int32)
+    const uint32_t Nu = (uint32_t)(N < 0x80000000LL ? N : 0x80000000LL);
     // every read is issued before any is used (indices clamped into the
     // list, the entries beyond it discarded after)
 #pragma unroll
@@ -260,7 +262,7 @@ __device__ int compact_list(const LDS_AS int32_t *lst, int K, int64_t N, int32_t
     for (int r = 0; r < MAXR; ++r) {
         const int k = k0 + r * 64 + lane;
         if (!(r * 64 < seg && k < K)) v[r] = -1;
-        mask[r] = __ballot(v[r] >= 0 && (int64_t)v[r] < N);
+        mask[r] = __ballot((uint32_t)v[r] < Nu);
         total += __popcll(mask[r]);
     }
     if (lane == 0) cnt[wid] = total;
@@ -804,7 +806,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
             const int e = slo + wid * IPW + k;
             const int v = slo < shi ? raw[e < shi ? e : slo] : -1;
             const int rw = __builtin_amdgcn_readfirstlane(v);
-            spec[k] = rw >= 0 && (int64_t)rw < p.N ? rw : -1;
+            spec[k] = (uint32_t)rw < (uint32_t)(p.N < 0x80000000LL ? p.N : 0x80000000LL) ? rw : -1;
         }
 #pragma unroll
         for (int k = 0; k < IPW; k += 4) {
