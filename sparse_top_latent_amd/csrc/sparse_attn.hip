@@ -81,6 +81,20 @@ constexpr float LOG2E = 1.4426950408889634f;
 // and denominator share the reference) is unchanged.
 constexpr float MAX_SLACK = 8.0f;
 
+// Division by a launch-constant d >= 1 of dividends 0 <= n < 2^31 as a
+// multiply and a shift: n / d == (n * m) >> k with l = ceil(log2 d),
+// k = 31 + l and m = ceil(2^k / d) < 2^32 (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994, Theorem 4.2
+// with N = 31 bits: 2^k <= m d <= 2^k + 2^l).  The host computes (m, k); on
+// the device it is three scalar instructions instead of a reciprocal
+// sequence, ahead of the kernels' first memory requests.
+struct Div32 {
+    uint32_t m, k;
+};
+__host__ __device__ inline int udiv(int n, Div32 d) {
+    return (int)(((uint64_t)(uint32_t)n * d.m) >> d.k);
+}
+
 struct FwdParams {
     const uint16_t *q;
     // Rows: index j < W is row j of the first source (rows_a rows per
@@ -103,6 +117,7 @@ struct FwdParams {
     int64_t N;
     int32_t T, H, K;
     int32_t S, HG, units, per_xcd, bs;  // see unit_of
+    Div32 dv_bs, dv_S, dv_HG, dv_T;      // division by bs, S, HG and T
     float qk_scale_log2;  // scale * log2(e)
     // f3: the output's last rd dims rotated back, pair i of query (b, t) by
     // rope[t, i] = (cos, sin) (rd = 0: none)
@@ -157,9 +172,10 @@ __device__ __forceinline__ int query_splits(int n, int K, int S) {
 // queries share an XCD's L2, while every XCD gets a share of every part of
 // the batch.  Units run in reverse order: in causal prefill the late queries
 // have the longest lists, and starting them first shortens the tail.
-__device__ __forceinline__ int unit_of(int bid, int units, int bs) {
+__device__ __forceinline__ int unit_of(int bid, int units, int bs, Div32 dv_bs) {
     const int x = bid & 7, j = bid >> 3;
-    const int u = ((j / bs) * 8 + x) * bs + (j % bs);
+    const int jb = udiv(j, dv_bs);
+    const int u = (jb * 8 + x) * bs + (j - jb * bs);
     return u < units ? units - 1 - u : -1;
 }
 
@@ -689,13 +705,14 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
                   "the host's LDS figure matches the declarations");
 
     const int bid = blockIdx.x;
-    const int unit = unit_of(bid, p.units, p.bs);
+    const int unit = unit_of(bid, p.units, p.bs, p.dv_bs);
     if (unit < 0) return;
-    // workgroup- and wave-uniform values in scalar registers
-    const int s = __builtin_amdgcn_readfirstlane(unit % p.S);
-    const int hg = __builtin_amdgcn_readfirstlane((unit / p.S) % p.HG);
-    const int qi = __builtin_amdgcn_readfirstlane(unit / (p.S * p.HG));
-    const int b = __builtin_amdgcn_readfirstlane(qi / p.T);
+    // workgroup- and wave-uniform values, in scalar registers
+    const int us = udiv(unit, p.dv_S);
+    const int s = unit - us * p.S;
+    const int qi = udiv(us, p.dv_HG);
+    const int hg = us - qi * p.HG;
+    const int b = udiv(qi, p.dv_T);
 
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hq = wid >> 1;      // head group of this wave
@@ -800,7 +817,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
     // that are not rows (< 0 or >= N) are never fetched.
     int spec[IPW];
     {
-        const int slo = (p.K * s) / p.S, shi = (p.K * (s + 1)) / p.S;  // K <= LIST_CAP
+        const int slo = udiv(p.K * s, p.dv_S), shi = udiv(p.K * (s + 1), p.dv_S);  // K <= LIST_CAP
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
             const int e = slo + wid * IPW + k;
@@ -1162,14 +1179,15 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     extern __shared__ int32_t list[];  // K entries: raw, then compacted in place
 
     const int bid = blockIdx.x;
-    const int unit = unit_of(bid, p.units, p.bs);
+    const int unit = unit_of(bid, p.units, p.bs, p.dv_bs);
     if (unit < 0) return;
-    // workgroup-uniform: kept in scalar registers (the divisions run on the
-    // vector unit), so the row and record base addresses below are scalar too
-    const int s = __builtin_amdgcn_readfirstlane(unit % p.S);
-    const int hg = __builtin_amdgcn_readfirstlane((unit / p.S) % p.HG);
-    const int qi = __builtin_amdgcn_readfirstlane(unit / (p.S * p.HG));
-    const int b = __builtin_amdgcn_readfirstlane(qi / p.T);
+    // workgroup-uniform values in scalar registers, so the row and record
+    // base addresses below are scalar too
+    const int us = udiv(unit, p.dv_S);
+    const int s = unit - us * p.S;
+    const int qi = udiv(us, p.dv_HG);
+    const int hg = us - qi * p.HG;
+    const int b = udiv(qi, p.dv_T);
 
     // the wave number is uniform: in a scalar register, so are the offsets it sets
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1510,12 +1528,12 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
     static_assert(sizeof(rbuf) + sizeof(pub) + sizeof(mbs) + sizeof(lbs) + sizeof(cnt) == hs_static_lds(D),
                   "the host's LDS figure matches the declarations");
 
-    const int unit = unit_of(blockIdx.x, p.units, p.bs);
+    const int unit = unit_of(blockIdx.x, p.units, p.bs, p.dv_bs);
     if (unit < 0) return;
-    // workgroup- and wave-uniform values in scalar registers
-    const int hg = __builtin_amdgcn_readfirstlane(unit % p.HG);
-    const int qi = __builtin_amdgcn_readfirstlane(unit / p.HG);
-    const int b = __builtin_amdgcn_readfirstlane(qi / p.T);
+    // workgroup- and wave-uniform values, in scalar registers
+    const int qi = udiv(unit, p.dv_HG);
+    const int hg = unit - qi * p.HG;
+    const int b = udiv(qi, p.dv_T);
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, li = lane & 15;
     const int h = hg * 16 + li;  // head of this lane (QK^T columns, softmax, outputs)
@@ -2449,6 +2467,21 @@ int check_common(const void *q, const void *kv, const int32_t *idxs, const sa_di
     return SA_OK;
 }
 
+// (m, k) of Div32 for a divisor 1 <= d < 2^31
+Div32 div32(int64_t d) {
+    uint32_t l = 0;
+    while (((int64_t)1 << l) < d) ++l;
+    const uint32_t k = 31 + l;
+    const uint64_t pw = (uint64_t)1 << k;
+    return Div32{(uint32_t)(pw / (uint64_t)d + (pw % (uint64_t)d != 0)), k};
+}
+void set_divisors(FwdParams &p) {
+    p.dv_bs = div32(p.bs > 0 ? p.bs : 1);
+    p.dv_S = div32(p.S > 0 ? p.S : 1);
+    p.dv_HG = div32(p.HG > 0 ? p.HG : 1);
+    p.dv_T = div32(p.T > 0 ? p.T : 1);
+}
+
 FwdParams make_params(const void *q, const void *kv, const float *sink, const int32_t *idxs,
                       float scale, void *out, const sa_dims *d, int S, void *ws) {
     FwdParams p{};
@@ -2484,6 +2517,7 @@ FwdParams make_params(const void *q, const void *kv, const float *sink, const in
     p.bs = (int32_t)bs;
     p.per_xcd = (int32_t)(((even + bs - 1) / bs) * bs);
     p.qk_scale_log2 = scale * LOG2E;
+    set_divisors(p);
     return p;
 }
 
@@ -2518,6 +2552,7 @@ hipError_t launch_hs(FwdParams p, const sa_dims *d, hipStream_t stream) {
     const int64_t bs = ((even + p.HG - 1) / p.HG) * p.HG;
     p.bs = (int32_t)bs;
     p.per_xcd = (int32_t)bs;
+    set_divisors(p);
     if (p.rec2 > 0)
         hipLaunchKernelGGL((attn_fwd_hs_kernel<512, true>), dim3(8 * p.per_xcd), dim3(512), lb, stream, p);
     else
