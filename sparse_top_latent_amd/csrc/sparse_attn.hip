@@ -1794,7 +1794,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                                                       uint16_t *__restrict__ out, int QH,
                                                       int H, int S, int per_xcd,
                                                       const float *__restrict__ rope, int rd,
-                                                      int T) {
+                                                      int T, Div32 dvH, Div32 dvT) {
     constexpr int LPR = D / 8;       // lanes per row
     constexpr int RPW = 64 / LPR;    // rows per wave
     constexpr int RWG = 4 * RPW;     // rows per workgroup
@@ -1814,7 +1814,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     const int sl = lane % LPR;               // lane within the row
     const int qh = wg * RWG + rw;
     const bool ok = qh < QH;                  // (no early exit: the row's lanes shuffle)
-    const int qi = ok ? qh / H : 0;
+    const int qi = ok ? udiv(qh, dvH) : 0;
     const int h = ok ? qh - qi * H : 0;
     const int c8 = sl * 8;
     const int64_t slot0 = (int64_t)qi * S * H + h;  // slot of split j: slot0 + j * H
@@ -1845,7 +1845,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     const bool rot = c8 >= D - rd;
     float4 cs0 = {1.f, 0.f, 1.f, 0.f}, cs1 = cs0;
     if (rd > 0) {
-        const float *f = rope + 2 * ((int64_t)(qi % T) * (rd / 2) + (rot ? (c8 - (D - rd)) / 2 : 0));
+        const float *f = rope + 2 * ((int64_t)(qi - udiv(qi, dvT) * T) * (rd / 2) + (rot ? (c8 - (D - rd)) / 2 : 0));
         const float4 r0 = *(const float4 *)f, r1 = *(const float4 *)(f + 4);
         if (rot) cs0 = r0, cs1 = r1;
     }
@@ -2410,10 +2410,19 @@ hipError_t launch_fwd_d(WgShape w, const FwdParams &p, hipStream_t stream) {
     return launch_fwd<D, 1, 2>(p, stream);
 }
 
+// (m, k) of Div32 for a divisor 1 <= d < 2^31
+Div32 div32(int64_t d) {
+    uint32_t l = 0;
+    while (((int64_t)1 << l) < d) ++l;
+    const uint32_t k = 31 + l;
+    const uint64_t pw = (uint64_t)1 << k;
+    return Div32{(uint32_t)(pw / (uint64_t)d + (pw % (uint64_t)d != 0)), k};
+}
 hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
                           const void *ws, const WsLayout &L, hipStream_t stream,
                           const float *rope = nullptr, int rd = 0) {
     const int64_t QH = queries(d) * d->H;
+    const Div32 dvH = div32(d->H), dvT = div32(d->T > 0 ? d->T : 1);
     const int rwg = 4 * (64 / (d->D / 8));  // rows per workgroup
     const int64_t wgs = (QH + rwg - 1) / rwg;
     const int per_xcd = (int)((wgs + 7) / 8);
@@ -2425,7 +2434,7 @@ hipError_t launch_combine(const sa_dims *d, int S, const float *sink, void *out,
     const int32_t *wp = (const int32_t *)((const uint8_t *)ws + L.plan_off);
     uint16_t *o = (uint16_t *)out;
 #define SA_COMBINE(DD, SB) \
-    hipLaunchKernelGGL((combine_kernel<DD, SB>), dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, (int)QH, d->H, S, per_xcd, rope, rd, d->T)
+    hipLaunchKernelGGL((combine_kernel<DD, SB>), dim3(grid), dim3(256), 0, stream, wo, wm, wl, wx, wp, sink, o, (int)QH, d->H, S, per_xcd, rope, rd, d->T, dvH, dvT)
     const bool small = S <= 4;  // one batch of four holds every split
     switch (d->D) {
         case 128: if (small) SA_COMBINE(128, 4); else SA_COMBINE(128, 8); break;
@@ -2467,14 +2476,6 @@ int check_common(const void *q, const void *kv, const int32_t *idxs, const sa_di
     return SA_OK;
 }
 
-// (m, k) of Div32 for a divisor 1 <= d < 2^31
-Div32 div32(int64_t d) {
-    uint32_t l = 0;
-    while (((int64_t)1 << l) < d) ++l;
-    const uint32_t k = 31 + l;
-    const uint64_t pw = (uint64_t)1 << k;
-    return Div32{(uint32_t)(pw / (uint64_t)d + (pw % (uint64_t)d != 0)), k};
-}
 void set_divisors(FwdParams &p) {
     p.dv_bs = div32(p.bs > 0 ? p.bs : 1);
     p.dv_S = div32(p.S > 0 ? p.S : 1);
