@@ -13,8 +13,12 @@ QK^T, sink softmax, PV and (with splits) the log-sum-exp combine.  Inputs are
 resident in HBM before timing; the timed steps cycle through ``--rotate``
 copies of q/kv/idxs at distinct addresses so that the rows a step gathers are
 not still sitting in the 256 MB Infinity Cache from the previous step (a
-second, labelled figure runs with one copy).  Each step is replayed from a
-captured HIP graph so that host launch overhead is not part of the time.
+second, labelled figure runs with one copy).  The timed steps are launched
+back to back on one stream while the GPU first runs a short sleep kernel, so
+that the host has queued them all before the first one starts and host launch
+cost is not part of the time; the same steps replayed from a captured HIP
+graph are reported beside them (``graph_replay``: on ROCm a graph adds time
+between its kernel nodes).
 
 Prints one JSON line.  ``value`` = queries per second of the headline workload.
 """
@@ -122,6 +126,12 @@ def gate(torch, ms=20.0):
     torch.cuda._sleep(int(ms * 1e-3 * 2.1e9))
 
 
+def gate_ms(calls):
+    """A sleep long enough for the host to queue `calls` calls (each well under
+    0.5 ms of host time, a few binding or torch launches)."""
+    return max(20.0, 0.5 * calls)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -144,10 +154,10 @@ def main():
     cap_stream = torch.cuda.Stream()
 
     def measure(w, R, warm_cache):
-        """Time one workload: ms per step (graph of R steps over R input
-        copies), optionally with one copy (warm cache), and the dominant
-        kernel alone on the stream it runs on.  Returns the figures and the
-        device inputs."""
+        """Time one workload: ms per step (back-to-back launches cycling
+        through R input copies; also replayed from a graph of R steps),
+        optionally with one copy (warm cache), and the dominant kernel alone
+        on the stream it runs on.  Returns the figures and the device inputs."""
         q0 = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
         kv0 = w.kv_device(dev)
         idx0 = torch.from_numpy(w.idxs).to(dev)
@@ -200,8 +210,20 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / args.steps
 
-        ms_step = timed(g_rot)
-        ms_step_warm = timed(g_warm) if g_warm is not None else None
+        def timed_eager(rotate):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            gate(torch, gate_ms(args.steps))
+            e0.record()
+            for k in range(args.steps):
+                step(k % R if rotate else 0)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+
+        ms_step = timed_eager(True)
+        ms_step_graph = timed(g_rot)
+        ms_step_warm = timed_eager(False) if warm_cache else None
 
         # the dominant kernel alone: back-to-back launches on the stream it
         # runs on (torch's current stream, where the binding launches)
@@ -252,6 +274,8 @@ def main():
         fig = {
             "ms_per_step": round(ms_step, 5),
             "value": round(Qn / t_step, 1),
+            "graph_replay": {"ms_per_step": round(ms_step_graph, 5),
+                             "value": round(Qn / (ms_step_graph * 1e-3), 1)},
             "config": {"workload": f"deepseek-v4.1-{w.name}", "B": w.B, "T": w.T, "H": w.H,
                        "D": w.D, "K": w.K, "N": w.N, "valid_entries": valid, "splits": S,
                        "input_copies_rotated": R},
@@ -300,28 +324,25 @@ def main():
         "path_roofline_frac": fig["path_roofline_frac"],
         "mfma_util": fig["mfma_util"],
         "warm_cache": fig["warm_cache"],
+        "graph_replay": fig["graph_replay"],
         "roofline": fig["roofline"],
     }
 
-    def time_graph(fn):
-        """ms per call of fn(i), replayed from a graph of R calls (one per copy)."""
+    def time_calls(fn):
+        """ms per call of fn(i), launched back to back over the R copies (as
+        the headline step)."""
         for i in range(R):
             fn(i)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap_stream):
-            for i in range(R):
-                fn(i)
-        g.replay()
         torch.cuda.synchronize()
-        gate(torch)
+        n = max(R, args.steps)
+        gate(torch, gate_ms(n))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(1, args.steps // R)
         e0.record()
-        for _ in range(reps):
-            g.replay()
+        for k in range(n):
+            fn(k % R)
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * R)
+        return e0.elapsed_time(e1) / n
 
     if args.two_source:
         # the rows as the model holds them: window rows and compressed rows in
@@ -337,8 +358,8 @@ def main():
         def cat(i):
             torch.cat([wins[i], cmps[i]], dim=1)
 
-        ms2 = time_graph(step2)
-        ms_cat = time_graph(cat)
+        ms2 = time_calls(step2)
+        ms_cat = time_calls(cat)
         line["two_source"] = {
             "window_rows": W, "ms_per_step": round(ms2, 5), "value": round(Qn / (ms2 * 1e-3), 1),
             "concat_copy_ms": round(ms_cat, 5),
@@ -358,7 +379,7 @@ def main():
             api.sparse_attn_2src_fp4(qs[i], wins4[i], recs[i], W, w.N, sink, idxs[i], w.scale,
                                      out=out, num_splits=S, workspace=ws)
 
-        ms4 = time_graph(step4)
+        ms4 = time_calls(step4)
         # algorithmic bytes: distinct window rows x 2D + distinct compressed rows x record
         nwin = sum(int(np.count_nonzero(np.asarray(r) < W)) for r in w.rows)
         ncmp = sum(int(np.count_nonzero(np.asarray(r) >= W)) for r in w.rows)
@@ -391,8 +412,8 @@ def main():
             y = torch.view_as_real(torch.view_as_complex(x) * fc)
             out[..., -rd:] = y.reshape(w.B, w.T, w.H, rd).to(torch.bfloat16)
 
-        ms_f = time_graph(fused)
-        ms_u = time_graph(unfused)
+        ms_f = time_calls(fused)
+        ms_u = time_calls(unfused)
         line["rope"] = {"rd": rd, "ms_per_step": round(ms_f, 5),
                         "value": round(Qn / (ms_f * 1e-3), 1),
                         "unfused_ms_per_step": round(ms_u, 5),
@@ -413,7 +434,7 @@ def main():
             scs = [torch.randn(Qk, Ck, generator=gen, device=dev) for _ in range(R)]
             lens = (torch.arange(1, Qk + 1, device=dev, dtype=torch.int32) // 2) if causal else None
             outk = torch.empty(Qk, TOPK, dtype=torch.int32, device=dev)
-            ms_k = time_graph(lambda i: api.topk(scs[i], TOPK, 128, lens=lens, out=outk))
+            ms_k = time_calls(lambda i: api.topk(scs[i], TOPK, 128, lens=lens, out=outk))
             nbytes = Qk * Ck * 4 + Qk * TOPK * 4 + (Qk * 4 if causal else 0)
             res[name] = {"queries": Qk, "candidates": Ck, "k": TOPK, "ms": round(ms_k, 5),
                          "GBps": round(nbytes / (ms_k * 1e-3) / 1e9, 1),
@@ -429,7 +450,7 @@ def main():
 
             # the rows picked here are random positions of kv, so the step
             # gathers the same number of rows as the benchmark step
-            ms_kd = time_graph(step_k)
+            ms_kd = time_calls(step_k)
             res["decode_with_attention"] = {"ms_per_step": round(ms_kd, 5),
                                             "value": round(Qn / (ms_kd * 1e-3), 1)}
         line["topk"] = res
@@ -441,7 +462,7 @@ def main():
         for name in OTHER_WORKLOADS:
             wo = wl.make(name)
             fo, so = measure(wo, R, warm_cache=False)
-            res[name] = {k: fo[k] for k in ("value", "ms_per_step", "gathered_kv_GBps",
+            res[name] = {k: fo[k] for k in ("value", "ms_per_step", "graph_replay", "gathered_kv_GBps",
                                              "path_roofline_frac", "mfma_util", "roofline")}
             res[name]["unit"] = "queries/s"
             res[name]["config"] = fo["config"]
