@@ -2110,8 +2110,14 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float *__restrict__ 
             key[4 * g + 2] = score_key(f.z), key[4 * g + 3] = score_key(f.w);
         }
     } else {  // slots past the visible length get key 0, taken off bin 0 below
+        // every load unconditional (past nv: the first visible score again,
+        // L > 0 here), so the thread's loads go out together and it waits once
+        const float *src = s + (nv > 0 ? base : 0);
+        float f[KPT];
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) key[j] = j < nv ? score_key(s[base + j]) : 0u;
+        for (int j = 0; j < KPT; ++j) f[j] = src[j < nv ? j : 0];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = j < nv ? score_key(f[j]) : 0u;
     }
     __syncthreads();
 
