@@ -465,6 +465,17 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, li = lane & 15;
     const int hbase = hg * HWG;
+    // the sink of every head tile requested before any is used (in a branch
+    // each, they would go out one memory round trip at a time)
+    const bool with_sink = p.S == 1 && p.sink != nullptr;
+    float zsv[NTL];
+    if (with_sink) {
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            const int h = hbase + 16 * t + li;
+            zsv[t] = p.sink[h < p.H ? h : 0];
+        }
+    }
     float inv[NTL];
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
@@ -472,10 +483,10 @@ __device__ __forceinline__ void store_outputs(const FwdParams &p, const f32x4_t 
         const int h = hbase + hl;
         const float ltot = lh[hl], mm = mh[hl];
         inv[t] = ltot > 0.f ? 1.f / ltot : 0.f;
-        if (p.S == 1 && p.sink != nullptr && h < p.H) {
+        if (with_sink && h < p.H) {
             // the sink joins the softmax: M = max(m, sink), L = l 2^(m-M) + 2^(sink-M);
             // nothing to attend to (m and the sink both -inf) gives 0
-            const float zs = p.sink[h] * LOG2E;
+            const float zs = zsv[t] * LOG2E;
             const float M = fmaxf(mm, zs);
             const float alpha = mm == -INFINITY ? 0.f : exp2_fast(mm - M);
             inv[t] = M == -INFINITY ? 0.f : alpha / (ltot * alpha + exp2_fast(zs - M));
