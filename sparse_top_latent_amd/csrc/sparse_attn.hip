@@ -1082,23 +1082,27 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         // rescales the accumulators (1 when the max stayed).
 #pragma unroll
         for (int t = 0; t < HT; ++t) {
+            // (scaled in place and masked in place in the list's last chunk,
+            // so that both cases share registers; the max is only formed when
+            // some score beats the kept one by more than MAX_SLACK)
             float sv[8];
-            if (cnt_c == KC) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][t][e & 3] * p.qk_scale_log2;
-            } else {
+            for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][t][e & 3] * p.qk_scale_log2;
+            if (cnt_c != KC) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = 16 * (e >> 2) + 4 * g + (e & 3);
-                    sv[e] = j < cnt_c ? sacc[e >> 2][t][e & 3] * p.qk_scale_log2 : -INFINITY;
-                }
+                for (int e = 0; e < 8; ++e)
+                    if (16 * (e >> 2) + 4 * g + (e & 3) >= cnt_c) sv[e] = -INFINITY;
             }
-            float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                               fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            const float th = m[t] + MAX_SLACK;
+            bool over = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) over |= sv[e] > th;
             float alpha = 1.f;
-            if (__ballot(lmax > m[t] + MAX_SLACK)) {
+            if (__ballot(over)) {
+                const float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
                 const float cmax = max_rows4(lmax);
-                const bool raise = cmax > m[t] + MAX_SLACK;
+                const bool raise = cmax > th;
                 const float mnew = raise ? cmax : m[t];
                 alpha = exp2_fast(m[t] - mnew);
                 lsum[t] *= alpha;
