@@ -1380,24 +1380,26 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
         }
         if (do_stage && c + 2 < nchunks) next_rows = rows_of(c + 2);
 
-        // a5: online softmax of the own tile (lazy max, as in attn_fwd_kernel)
+        // a5: online softmax of the own tile (lazy max, as in attn_fwd_kernel:
+        // scaled and tail-masked in place, the max formed only when needed)
         float sv[8];
-        if (cnt_c == KC) {  // a full chunk: nothing to mask (uniform branch)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3] * p.qk_scale_log2;
-        } else {
+        for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3] * p.qk_scale_log2;
+        if (cnt_c != KC) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = 16 * (e >> 2) + 4 * g + (e & 3);
-                sv[e] = j < cnt_c ? sacc[e >> 2][e & 3] * p.qk_scale_log2 : -INFINITY;
-            }
+            for (int e = 0; e < 8; ++e)
+                if (16 * (e >> 2) + 4 * g + (e & 3) >= cnt_c) sv[e] = -INFINITY;
         }
-        const float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                                 fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        const float th = m + MAX_SLACK;
+        bool over = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) over |= sv[e] > th;
         float alpha = 1.f;
-        if (__ballot(lmax > m + MAX_SLACK)) {
+        if (__ballot(over)) {
+            const float lmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
             const float cmax = max_rows4(lmax);
-            const float mnew = cmax > m + MAX_SLACK ? cmax : m;
+            const float mnew = cmax > th ? cmax : m;
             alpha = exp2_fast(m - mnew);
             lsum *= alpha;
             m = mnew;
