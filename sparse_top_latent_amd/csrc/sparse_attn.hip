@@ -237,6 +237,13 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// lo + hi of a packed pair of bf16 values, plus acc, in one v_dot2_f32_bf16
+// (dot product with (1, 1); the products are exact).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
 // Two floats to two fp16 (round to nearest even), low half first.
 __device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
@@ -1120,8 +1127,7 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) pv[e] = exp2_fast(own[e] - m[t]);
             const u32x2_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3])};
-            lsum[t] += __uint_as_float(pw[0] << 16) + __uint_as_float(pw[0] & 0xffff0000u) +
-                       __uint_as_float(pw[1] << 16) + __uint_as_float(pw[1] & 0xffff0000u);
+            lsum[t] = add_bf16_pair(pw[1], add_bf16_pair(pw[0], lsum[t]));
             pbuf[hq * HT + t][dh][lane] = pw;
             if (dh == 0 && g == 0) abuf[hq * HT + t][li] = alpha;
         }
@@ -1408,11 +1414,8 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
                             pack2_bf16(exp2_fast(sv[2] - m), exp2_fast(sv[3] - m)),
                             pack2_bf16(exp2_fast(sv[4] - m), exp2_fast(sv[5] - m)),
                             pack2_bf16(exp2_fast(sv[6] - m), exp2_fast(sv[7] - m))};
-        float psum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            psum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
-        lsum += psum;
+        for (int e = 0; e < 4; ++e) lsum = add_bf16_pair(pw[e], lsum);
 
         // every wave publishes its tile's weights and rescale factor
         xp[wid][lane] = pw;
