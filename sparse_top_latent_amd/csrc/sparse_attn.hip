@@ -863,8 +863,10 @@ __global__ __launch_bounds__(NHQ * 128) void attn_fwd_kernel(FwdParams p) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         return;
     }
-    const int lo = (n * s) / Sq;  // n <= LIST_CAP and s < MAX_SPLITS: no overflow
-    const int hi = (n * (s + 1)) / Sq;
+    // n <= LIST_CAP and s < MAX_SPLITS: no overflow; a query with every entry
+    // valid uses all S slots, and the host's divisor by S serves
+    const int lo = Sq == p.S ? udiv(n * s, p.dv_S) : (n * s) / Sq;
+    const int hi = Sq == p.S ? udiv(n * (s + 1), p.dv_S) : (n * (s + 1)) / Sq;
     const int nchunks = (hi - lo + KC - 1) / KC;
 
     // Tail slots repeat the chunk's first row; their scores are masked to
@@ -1237,8 +1239,10 @@ __global__ __launch_bounds__(NHQ * 128, 2) void attn_fwd_mq_kernel(FwdParams p) 
     const int Sq = query_splits(n, p.K, p.S);  // a10
     if (p.S > 1 && s == 0 && hg == 0 && tid == 0) p.ws_plan[qi] = Sq;
     if (s >= Sq) return;  // a spare split slot
-    const int lo = (n * s) / Sq;  // n <= LIST_CAP and s < MAX_SPLITS: no overflow
-    const int hi = (n * (s + 1)) / Sq;
+    // n <= LIST_CAP and s < MAX_SPLITS: no overflow; a query with every entry
+    // valid uses all S slots, and the host's divisor by S serves
+    const int lo = Sq == p.S ? udiv(n * s, p.dv_S) : (n * s) / Sq;
+    const int hi = Sq == p.S ? udiv(n * (s + 1), p.dv_S) : (n * (s + 1)) / Sq;
     const int nchunks = (hi - lo + KC - 1) / KC;
 
     // a2: chunk c (KC rows) into ring slot c % NB, one row per DMA
