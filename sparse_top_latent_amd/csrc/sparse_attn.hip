@@ -1804,8 +1804,10 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
 // LPR = D/8 lanes own one output row (8 columns each), so a wave merges
 // 64/LPR rows and a workgroup 4x that.  The first SB splits of the rows and
 // every (m, l, x) of the lane's row are requested before anything is waited
-// for, so the merge costs about one memory round trip.  The factors go through
-// a small LDS table (one per row).  Workgroups are laid out so that the rows
+// for, so the merge costs about one memory round trip.  The max and the
+// denominator are reduced over the row's lanes on the VALU; each split's
+// factor is then read from the lane that holds it (a row per wave, D = 512)
+// or through a small LDS table (D < 512).  Workgroups are laid out so that the rows
 // of a query are merged on the XCD whose workgroups wrote its partials (the
 // same blockIdx-to-XCD order as attn_fwd), where they may still sit in L2.
 template <int D, int SB>
