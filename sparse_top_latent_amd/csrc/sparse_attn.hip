@@ -1569,15 +1569,17 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
     // row); FP4 build, j >= W: of its record, lanes past the record reading
     // its last 16 bytes again (unused).  Every lane loads, so no load sits in a
     // lane-dependent branch and the compiler can count them.
+    // (row numbers and W are below 2^31: the source test is a 32-bit scalar compare)
+    const int Wc = (int)(p.W < 0x7FFFFFFF ? p.W : 0x7FFFFFFF);
     auto row_src = [&](int j) {
-        if (FP4 && j >= p.W)
+        if (FP4 && j >= Wc)
             return (const u32x4_t *)(recb + (int64_t)j * p.rec2 + (lane * 16 < p.rec2 ? lane * 16 : p.rec2 - 16));
-        return (const u32x4_t *)((j < p.W ? kva : kvb2) + (int64_t)j * D) + lane;
+        return (const u32x4_t *)((j < Wc ? kva : kvb2) + (int64_t)j * D) + lane;
     };
     auto load_row = [&](int j, u32x4_t &dst) { dst = *row_src(j); };
     // row j into position r of a round buffer (a record where expand_fp4_own reads it)
     auto write_row = [&](LDS_AS uint8_t *Lb, int r, int j, const u32x4_t &v) {
-        if (!FP4 || j < p.W)
+        if (!FP4 || j < Wc)
             *(LDS_AS u32x4_t *)(Lb + r * RS + lane * 16) = v;
         else if (lane * 16 < p.rec2)
             *(LDS_AS u32x4_t *)(Lb + r * RS + ((r & 1) ? 0 : RS - p.rec2) + lane * 16) = v;
@@ -1677,9 +1679,7 @@ __global__ __launch_bounds__(512) void attn_fwd_hs_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[i] = sv[i] == -INFINITY ? 0.f : exp2_fast(sv[i] - mb);
         const u32x2_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3])};
-        float ps = __uint_as_float(pw[0] << 16) + __uint_as_float(pw[0] & 0xffff0000u) +
-                   __uint_as_float(pw[1] << 16) + __uint_as_float(pw[1] & 0xffff0000u);
-        ps = sum_rows4(ps);
+        const float ps = sum_rows4(add_bf16_pair(pw[1], add_bf16_pair(pw[0], 0.f)));
         pub[pbi][wid][lane] = pw;
         if (g == 0) {
             mbs[pbi][wid][li] = mb;
